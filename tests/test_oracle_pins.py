@@ -1,0 +1,278 @@
+"""Pins of the float64 oracle to things other than itself.
+
+Each test checks the oracle against a number the pages print (tests/golden/),
+a closed form, an invariant of the mathematics, a brute-force computation on
+tiny inputs, or an independent library routine.  test_oracle_mutations.py
+plants plausible mistakes in the oracle and checks that these pins catch them.
+"""
+
+import collections
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.ckv_oracle as O
+from tests.conftest import read_page_numbers, read_window_counts
+
+RNG = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- shapes --
+
+def test_rope_band_widths_printed():
+    pn = read_page_numbers()
+    assert list(O.rope_bands(128)) == pn["rope_bands_d128"]
+    assert sum(O.rope_bands(128)) == 128
+    # head_dim 64 (tiny config): same rule, bands must still tile the head.
+    assert sum(O.rope_bands(64)) == 64 and all(b % 2 == 0 for b in O.rope_bands(64))
+
+
+def test_latent_shape_and_tokens_worked_example():
+    pn = read_page_numbers()
+    shape = O.latent_shape(81, 720, 1280, (4, 8, 8), 16)
+    assert list(shape) == pn["latent_shape_81f_1280x720"]
+    assert O.latent_frames(81) == pn["latent_frames_81"][0]
+    per_frame = O.tokens_per_frame(shape[2], shape[3])
+    assert per_frame == pn["tokens_per_frame_720p_a14b"][0]
+    assert per_frame * shape[1] == pn["tokens_total_720p_a14b"][0]
+    with pytest.raises(ValueError):
+        O.latent_frames(80)
+
+
+def test_5b_profile_token_counts_consistent():
+    """1280x704 through the 5B VAE (4x16x16) and 2x2 patchify gives 22 x 40 =
+    880 tokens per latent frame; 121 video frames are 31 latent frames = a
+    3-frame first chunk plus 28 one-frame chunks = 29 chunks."""
+    pn = read_page_numbers()
+    w, h = (int(x) for x in pn["profile_width_height"])
+    assert [w, h] == [int(x) for x in pn["ti2v_720p_width_height"]]
+    st, sh, sw = (int(x) for x in pn["vae_stride_5b"])
+    comp = [int(x) for x in pn["compression_with_patchify_5b"]]
+    assert comp == [st, 2 * sh, 2 * sw]
+    z = O.latent_shape(int(pn["video_frames_5b"][0]), h, w, (st, sh, sw), 48)
+    assert O.tokens_per_frame(z[2], z[3]) == 880 == 22 * 40
+    f0 = int(pn["profile_first_chunk_frames"][0])
+    later = int(pn["profile_later_chunk_frames"][0])
+    chunks = int(pn["profile_chunks"][0])
+    assert z[1] == 31 == f0 + (chunks - 1) * later
+    assert O.chunk_tokens(0, 22, 40, f0) == 2640
+    assert O.chunk_tokens(5, 22, 40, f0) == 880
+
+
+def test_flop_formula_worked_example():
+    pn = read_page_numbers()
+    flops = O.attention_flops(75600, 75600, 5120)
+    assert float(f"{flops:.3g}") == pn["attention_flops_layer_a14b"][0]
+
+
+def test_token_positions_brute_force():
+    """Frame-major, then row, then column; absolute frame index."""
+    gh, gw, f0 = 3, 5, 3
+    for c in (0, 1, 4):
+        pos = O.token_positions(c, gh, gw, f0)
+        frames = range(0, f0) if c == 0 else [f0 + c - 1]
+        expect = [(f, h, w) for f in frames for h in range(gh) for w in range(gw)]
+        assert pos.tolist() == [list(t) for t in expect]
+
+
+# ------------------------------------------------------------------ RoPE --
+
+def _rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+def test_rope_is_complex_multiplication():
+    """Adjacent pairs are complex numbers multiplied by e^{i angle}."""
+    x = _rand(7, 3, 128)
+    pos = RNG.integers(0, 30, size=(7, 3))
+    ang = O.rope_angles(pos, 128, 10000.0)
+    z = x[:, :, 0::2] + 1j * x[:, :, 1::2]
+    zr = z * np.exp(1j * ang)[:, None, :]
+    got = O.rope3d(x, pos, 10000.0)
+    np.testing.assert_allclose(got[:, :, 0::2], zr.real, atol=1e-13)
+    np.testing.assert_allclose(got[:, :, 1::2], zr.imag, atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_band_layout(d):
+    """A position on one axis rotates exactly that axis' band of dims:
+    time first, then height, then width."""
+    dt, dh, dw = O.rope_bands(d)
+    x = _rand(1, 2, d)
+    edges = {0: (0, dt), 1: (dt, dt + dh), 2: (dt + dh, d)}
+    for axis in range(3):
+        pos = np.zeros((1, 3), dtype=np.int64)
+        pos[0, axis] = 5
+        y = O.rope3d(x, pos, 10000.0)
+        lo, hi = edges[axis]
+        changed = np.abs(y - x).max(axis=(0, 1)) > 1e-12
+        assert changed[lo:hi].all(), (axis, lo, hi)
+        assert not changed[:lo].any() and not changed[hi:].any()
+
+
+def test_rope_identity_at_origin_and_norm():
+    x = _rand(5, 2, 128)
+    np.testing.assert_array_equal(O.rope3d(x, np.zeros((5, 3)), 10000.0), x)
+    pos = RNG.integers(0, 1000, size=(5, 3))
+    y = O.rope3d(x, pos, 10000.0)
+    np.testing.assert_allclose(y[..., 0::2] ** 2 + y[..., 1::2] ** 2,
+                               x[..., 0::2] ** 2 + x[..., 1::2] ** 2, rtol=1e-12)
+
+
+def test_rope_relative_position_property():
+    """<R_a q, R_b k> = <q, R_{b-a} k>: the score depends only on the
+    coordinate difference ("3D RoPE" section)."""
+    q, k = _rand(6, 1, 128), _rand(6, 1, 128)
+    a = RNG.integers(0, 40, size=(6, 3))
+    b = RNG.integers(0, 40, size=(6, 3))
+    lhs = np.einsum("nhd,nhd->n", O.rope3d(q, a, 10000.0), O.rope3d(k, b, 10000.0))
+    rhs = np.einsum("nhd,nhd->n", q, O.rope3d(k, b - a, 10000.0))
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-11, atol=1e-11)
+
+
+def test_attention_shift_invariance_through_rope():
+    """Shifting every token by the same (df, dh, dw) leaves attention unchanged."""
+    q, k, v = _rand(5, 2, 64), _rand(9, 2, 64), _rand(9, 2, 64)
+    pq = RNG.integers(0, 20, size=(5, 3))
+    pk = RNG.integers(0, 20, size=(9, 3))
+    shift = np.array([[7, -3, 11]])
+    o1 = O.attend(O.rope3d(q, pq, 1e4), O.rope3d(k, pk, 1e4), v, 0.125)
+    o2 = O.attend(O.rope3d(q, pq + shift, 1e4), O.rope3d(k, pk + shift, 1e4), v, 0.125)
+    np.testing.assert_allclose(o1, o2, atol=1e-10)
+
+
+# ----------------------------------------------------------------- window --
+
+def _deque_windows(num_chunks, window):
+    """Brute-force simulation: keep the last `window` noisy chunks in a FIFO;
+    chunk 0 never enters it (it is only the sink); each chunk reads the FIFO
+    before its own entry is appended."""
+    hist = collections.deque(maxlen=window) if window > 0 else None
+    out = {}
+    for c in range(num_chunks):
+        out[c] = list(hist) if (hist is not None and c >= 1) else []
+        if c >= 1 and hist is not None:
+            hist.append(c)
+    return out
+
+
+@pytest.mark.parametrize("window", [0, 1, 2, 5, 18, 40])
+def test_window_matches_fifo_simulation(window):
+    sim = _deque_windows(60, window)
+    for c in range(60):
+        assert O.window_chunks(c, window) == sim[c]
+        assert 0 not in O.window_chunks(c, window)  # no duplication of chunk 0
+
+
+def test_window_golden():
+    windows, keys = read_window_counts()
+    for (w, c), ids in windows.items():
+        assert O.window_chunks(c, w) == ids, (w, c)
+    for (gh, gw, f0, w, c), n in keys.items():
+        assert O.window_key_count(c, w, gh, gw, f0) == n, (gh, gw, f0, w, c)
+
+
+def test_window_no_eviction_when_window_covers_history():
+    for c in range(1, 29):
+        assert O.window_chunks(c, 28) == list(range(1, c))
+
+
+# -------------------------------------------------------------- attention --
+
+def test_single_key_returns_its_value():
+    q, k, v = _rand(4, 3, 64), _rand(1, 3, 64), _rand(1, 3, 64)
+    o = O.attend(q, k, v, 0.125)
+    np.testing.assert_array_equal(o, np.broadcast_to(v, o.shape))
+
+
+def test_zero_query_returns_mean_value():
+    k, v = _rand(13, 2, 64), _rand(13, 2, 64)
+    o = O.attend(np.zeros((3, 2, 64)), k, v, 0.125)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-14)
+
+
+def test_key_permutation_invariance():
+    q, k, v = _rand(4, 2, 64), _rand(17, 2, 64), _rand(17, 2, 64)
+    perm = RNG.permutation(17)
+    np.testing.assert_allclose(O.attend(q, k, v, 0.2), O.attend(q, k[perm], v[perm], 0.2), atol=1e-13)
+
+
+def test_segment_merge_equals_whole():
+    """Softmax over a concatenation = log-sum-exp weighted merge of the
+    per-segment softmaxes (what a split-key kernel relies on)."""
+    q = _rand(3, 2, 32)
+    segs = [(_rand(n, 2, 32), _rand(n, 2, 32)) for n in (5, 1, 9)]
+    k = np.concatenate([s[0] for s in segs])
+    v = np.concatenate([s[1] for s in segs])
+    whole = O.attend(q, k, v, 0.3)
+    num = 0
+    den = 0
+    for ks, vs in segs:
+        z = 0.3 * np.einsum("qhd,khd->qhk", q, ks)
+        lse = np.log(np.exp(z).sum(-1))                    # [q, h]
+        num = num + np.exp(lse)[..., None] * O.attend(q, ks, vs, 0.3)
+        den = den + np.exp(lse)[..., None]
+    np.testing.assert_allclose(whole, num / den, atol=1e-13)
+
+
+def test_brute_force_loops_tiny():
+    nq, nk, nh, d = 3, 5, 2, 4
+    q, k, v = _rand(nq, nh, d), _rand(nk, nh, d), _rand(nk, nh, d)
+    scale = 0.7
+    o = O.attend(q, k, v, scale)
+    for i, h in itertools.product(range(nq), range(nh)):
+        z = [scale * sum(q[i, h, t] * k[j, h, t] for t in range(d)) for j in range(nk)]
+        e = [math.exp(x) for x in z]
+        s = sum(e)
+        for t in range(d):
+            ref = sum(e[j] / s * v[j, h, t] for j in range(nk))
+            assert abs(o[i, h, t] - ref) < 1e-12
+
+
+def test_matches_torch_sdpa_float64():
+    q, k, v = _rand(33, 4, 64), _rand(70, 4, 64), _rand(70, 4, 64)
+    scale = 1.0 / 8.0
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), torch.from_numpy(k).permute(1, 0, 2),
+        torch.from_numpy(v).permute(1, 0, 2), scale=scale).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(O.attend(q, k, v, scale), ref, atol=1e-12)
+
+
+# --------------------------------------------------------------- rollout --
+
+def test_rollout_window_assembly_tiny():
+    """Tiny rollout: the keys a chunk attends to are exactly sink, the window's
+    same-step entries and its own, in that order; steps do not mix."""
+    cfg = O.OracleConfig(1, 2, 1, 64, 4, 4, 3, 2, 6)
+    ro = O.OracleRollout(cfg)
+    mk = lambda n, tag: np.full((n, 1, 64), float(tag))  # noqa: E731
+    ro.sink_pass(0, mk(48, 0), mk(48, 0), mk(48, -1))
+    for c in range(1, 6):
+        for s in range(2):
+            tag = 10 * c + s
+            ro.chunk_step(0, s, c, mk(16, tag), mk(16, tag), mk(16, tag))
+            _, vw = ro.window_kv(0, s, c, mk(16, tag), mk(16, tag))
+            ids = [-1] * 48 + [10 * j + s for j in O.window_chunks(c, 2) for _ in range(16)] + [tag] * 16
+            assert vw[:, 0, 0].tolist() == [float(x) for x in ids]
+            assert vw.shape[0] == O.window_key_count(c, 2, 4, 4, 3)
+
+
+def test_rollout_chunk_step_matches_direct_definition():
+    cfg = O.OracleConfig(1, 1, 2, 64, 2, 4, 3, 2, 5)
+    ro = O.OracleRollout(cfg)
+    q0, k0, v0 = _rand(24, 2, 64), _rand(24, 2, 64), _rand(24, 2, 64)
+    ro.sink_pass(0, q0, k0, v0)
+    ks, vs = [O.rope3d(k0, cfg.positions(0), 1e4)], [v0]
+    for c in range(1, 5):
+        q, k, v = _rand(8, 2, 64), _rand(8, 2, 64), _rand(8, 2, 64)
+        o, _ = ro.chunk_step(0, 0, c, q, k, v)
+        kr = O.rope3d(k, cfg.positions(c), 1e4)
+        win_k = [ks[0]] + [ks[j] for j in O.window_chunks(c, 2)] + [kr]
+        win_v = [vs[0]] + [vs[j] for j in O.window_chunks(c, 2)] + [v]
+        ref = O.attend(O.rope3d(q, cfg.positions(c), 1e4), np.concatenate(win_k), np.concatenate(win_v), 0.125)
+        np.testing.assert_allclose(o, ref, atol=1e-13)
+        ks.append(kr)
+        vs.append(v)
