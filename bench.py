@@ -1,0 +1,282 @@
+"""Benchmark: same-step chunk attention over a full 29-chunk rollout on one GPU.
+
+One step = one 1-layer rollout of the 1280x704 profile through the C-ABI:
+chunk 0 (2640 tokens) for 4 denoising steps (RoPE + append, self-attention),
+its clean sink pass (sink build + self-attention), then chunks 1..28 (880
+tokens) x 4 steps (RoPE + ring append, chunk attention over sink + up to 18
+same-step chunks + itself); 24 heads x 128, bf16.  Inputs (fresh seeded
+N(0,1) q, k, v per chunk and step) are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is algorithmic attention TFLOP/s over the
+whole rollout (4 * n_q * n_k * 3072 per attention call, the convention of
+"Learning Video Generation from the Wan2.2 Source Code", Chapter 8);
+`ms_per_step` is milliseconds per rollout.  The roofline block is for the
+chunk-attention kernel on its 880-query x 19,360-key launches (chunks 19..28),
+timed with HIP events on the launch stream inside the timed rollouts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "chunk_attn_880x19360_counters.txt")
+ATTN_SOURCE = os.path.join(ROOT, "chunked_kv_attention_amd", "csrc", "chunk_attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def profile_config():
+    import chunked_kv_attention_amd as C
+    return C.Config(num_layers=1, num_steps=4, num_heads=24, head_dim=128, grid_h=22, grid_w=40,
+                    first_chunk_frames=3, window_chunks=18, max_chunks=29)
+
+
+def rollout_calls(cfg):
+    """(kind, step, chunk) in rollout order: chunk 0's steps, its sink pass,
+    then chunks 1.. x steps."""
+    calls = [("first", s, 0) for s in range(cfg.num_steps)] + [("sink", -1, 0)]
+    calls += [("chunk", s, c) for c in range(1, cfg.max_chunks) for s in range(cfg.num_steps)]
+    return calls
+
+
+def keys_of(cfg, chunk):
+    n0, n1 = cfg.tokens(0), cfg.tokens(1)
+    if chunk == 0:
+        return n0
+    return n0 + n1 * min(chunk - 1, cfg.window_chunks) + n1
+
+
+def attn_flops(cfg, chunk):
+    return 4 * cfg.tokens(chunk) * keys_of(cfg, chunk) * cfg.num_heads * cfg.head_dim
+
+
+def read_counters():
+    """HBM traffic per launch from committed rocprofv3 counter runs, valid only
+    while the kernel source is unchanged."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    for line in open(COUNTERS_FILE):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if vals.get("source_sha256") != src or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(cfg, heads):
+    """The float64 oracle, untuned, on a bounded sample of the same workload:
+    the rotation of the window's keys (sink + chunks 1..18) and of chunk 19's
+    q/k, then chunk 19's attention (880 queries x 19,360 keys) for `heads`
+    heads.  Rate = that attention's algorithmic FLOPs / wall time."""
+    import numpy as np
+
+    import oracle.ckv_oracle as O
+    from chunked_kv_attention_amd import inputs as I
+
+    ocfg = O.OracleConfig(1, cfg.num_steps, heads, cfg.head_dim, cfg.grid_h, cfg.grid_w,
+                          cfg.first_chunk_frames, cfg.window_chunks, cfg.max_chunks)
+    ro = O.OracleRollout(ocfg)
+    data = {}
+    for c in range(0, 20):
+        n = cfg.tokens(c)
+        data[c] = [I.bf16_bits_to_f64(b) for b in
+                   I.draw_qkv_bits(n, heads, cfg.head_dim, base_seed=0, chunk=c, step_code=4 if c == 0 else 0)]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    ro.sink[0] = (ro.rotate(0, data[0][1]), data[0][2])
+    for c in range(1, 19):
+        ro.noisy[(0, 0, c)] = (ro.rotate(c, data[c][1]), data[c][2])
+    out, _ = ro.chunk_step(0, 0, 19, *data[19])
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    flops = 4 * cfg.tokens(19) * keys_of(cfg, 19) * heads * cfg.head_dim
+    cpu_model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": (f"float64 numpy oracle: RoPE of the window's keys (sink + chunks 1..18) and chunk 19's "
+                   f"q/k, then chunk 19's attention 880 x 19,360 keys for {heads} of 24 heads; "
+                   f"{flops / 1e9:.1f} GFLOP in {dt:.2f} s"),
+        "seconds": dt, "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the same-step chunk attention path is built and timed on a single "
+              "MI355X (head-sharding across GPUs is a design note, not part of this build). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_kv_attention_amd as C
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    C.load()
+    dev = torch.device("cuda:0")
+    cfg = profile_config()
+    H, d = cfg.num_heads, cfg.head_dim
+    calls = rollout_calls(cfg)
+
+    # Inputs: fresh seeded N(0,1) q, k, v for every call, resident in HBM.
+    gen = torch.Generator(device=dev)
+    inputs = {}
+    for i, (kind, step, chunk) in enumerate(calls):
+        n = cfg.tokens(chunk)
+        gen.manual_seed(1000 + i)
+        inputs[i] = [torch.randn((n, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                     for _ in range(3)]
+    q_rot = {n: torch.empty((n, H, d), device=dev, dtype=torch.bfloat16) for n in (cfg.tokens(0), cfg.tokens(1))}
+    out = {n: torch.empty((n, H, d), device=dev, dtype=torch.bfloat16) for n in (cfg.tokens(0), cfg.tokens(1))}
+    cache = C.Cache(cfg)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    total_flops = sum(attn_flops(cfg, c) for _, _, c in calls)
+    big = [i for i, (kind, _, c) in enumerate(calls) if kind == "chunk" and keys_of(cfg, c) == 19360]
+    append_idx = [i for i, (kind, _, c) in enumerate(calls) if kind == "chunk"]
+
+    def run_rollout(events=None):
+        cache.reset()
+        for i, (kind, step, chunk) in enumerate(calls):
+            q, k, v = inputs[i]
+            n = q.shape[0]
+            ev = events[i] if events is not None else None
+            if ev is not None:
+                ev[0].record(stream)
+            if kind == "sink":
+                cache.sink_build(0, q, k, v, q_rot[n], stream=stream)
+            else:
+                cache.rope_append(0, step, chunk, q, k, v, q_rot[n], stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            cache.chunk_attention(0, C.STEP_SINK if kind == "sink" else step, chunk, q_rot[n], out[n],
+                                  stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        run_rollout()
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        run_rollout(events[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    attn_big_ms = [events[k][i][1].elapsed_time(events[k][i][2]) for k in range(args.steps) for i in big]
+    attn_all_ms = sum(events[k][i][1].elapsed_time(events[k][i][2]) for k in range(args.steps)
+                      for i in range(len(calls)))
+    append_ms = [events[k][i][0].elapsed_time(events[k][i][1]) for k in range(args.steps) for i in append_idx]
+    big_flops = attn_flops(cfg, 19)
+    big_us = 1e3 * sum(attn_big_ms) / len(attn_big_ms)
+    big_tflops = big_flops / (big_us * 1e-6) / 1e12
+    append_bytes = 6 * cfg.tokens(1) * H * d * 2
+    append_us = 1e3 * sum(append_ms) / len(append_ms)
+    traffic = read_counters()
+
+    result = {
+        "metric": "same-step chunk-attn TFLOP/s + % bf16 MFMA peak; ms per 29-chunk rollout",
+        "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "1-layer 29-chunk same-step rollout at 1280x704: chunk 0 = 2640 tokens x 4 steps + "
+                        "sink pass, chunks 1..28 = 880 tokens x 4 steps, window = sink + 18 same-step chunks "
+                        "+ self (<= 19,360 keys), 24 heads x 128",
+            "global_batch": 1,
+            "seq_len": 19360,
+            "parallelism": "none (1 GPU)",
+            "attention_calls_per_step": len(calls),
+            "algorithmic_tflop_per_step": round(total_flops / 1e12, 4),
+        },
+        "pct_bf16_peak": round(100 * total_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "chunk_attn_880x19360": {
+            "us_per_call": round(big_us, 2),
+            "tflops": round(big_tflops, 2),
+            "pct_bf16_peak": round(100 * big_tflops / PEAK_BF16_TFLOPS, 2),
+            "launches_timed": len(attn_big_ms),
+            "key_splits": cache.attention_splits(880, 19360),
+        },
+        "attention_share_of_step": round(attn_all_ms / total_ms, 4),
+        "rope_append_880": {
+            "us_per_call": round(append_us, 2),
+            "gbs": round(append_bytes / (append_us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * append_bytes / (append_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(big_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(big_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

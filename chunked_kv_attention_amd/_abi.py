@@ -1,0 +1,234 @@
+"""ctypes binding of libckv.so (include/ckv.h): argument marshalling only.
+
+Every operation runs in the HIP library; this module checks tensor shapes and
+dtypes, passes device pointers and the current HIP stream, and turns status
+codes into exceptions.  It raises if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libckv.so")
+
+CKV_OK, CKV_E_INVALID, CKV_E_ORDER, CKV_E_STATE, CKV_E_ARENA, CKV_E_HIP = range(6)
+STEP_SINK = -1
+
+# Every symbol include/ckv.h declares.
+EXPORTS = (
+    "ckv_cache_bytes", "ckv_cache_create", "ckv_cache_create_dry", "ckv_cache_reset",
+    "ckv_cache_destroy", "ckv_rope_append", "ckv_sink_build", "ckv_chunk_attention",
+    "ckv_window", "ckv_ring_slot", "ckv_debug_copy_kv", "ckv_attention_splits",
+    "ckv_status_string",
+)
+
+
+class CkvConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("num_steps", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("grid_h", ctypes.c_int32),
+        ("grid_w", ctypes.c_int32),
+        ("first_chunk_frames", ctypes.c_int32),
+        ("window_chunks", ctypes.c_int32),
+        ("max_chunks", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("softmax_scale", ctypes.c_float),
+        ("reserved1", ctypes.c_int32),
+    ]
+
+
+assert ctypes.sizeof(CkvConfig) == 56
+
+
+class CkvSegment(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("kind", "first_slot", "chunk_first", "n_chunks", "n_tokens")]
+
+
+class CkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libckv.so once; raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m chunked_kv_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(CkvConfig)
+    sig = {
+        "ckv_cache_bytes": (SZ, [cfgp]),
+        "ckv_cache_create": (I32, [cfgp, P, SZ, ctypes.POINTER(P)]),
+        "ckv_cache_create_dry": (I32, [cfgp, ctypes.POINTER(P)]),
+        "ckv_cache_reset": (I32, [P]),
+        "ckv_cache_destroy": (I32, [P]),
+        "ckv_rope_append": (I32, [P, I32, I32, I32, P, P, P, P, P]),
+        "ckv_sink_build": (I32, [P, I32, P, P, P, P, P]),
+        "ckv_chunk_attention": (I32, [P, I32, I32, I32, P, P, P]),
+        "ckv_window": (I32, [P, I32, I32, I32, ctypes.POINTER(CkvSegment), I32, ctypes.POINTER(I32)]),
+        "ckv_ring_slot": (I32, [P, I32, ctypes.POINTER(I32)]),
+        "ckv_debug_copy_kv": (I32, [P, I32, I32, I32, P, P, P]),
+        "ckv_attention_splits": (I32, [P, I32, I32]),
+        "ckv_status_string": (ctypes.c_char_p, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(st: int) -> str:
+    return load().ckv_status_string(int(st)).decode()
+
+
+@dataclass(frozen=True)
+class Config:
+    num_layers: int
+    num_steps: int
+    num_heads: int
+    head_dim: int
+    grid_h: int
+    grid_w: int
+    first_chunk_frames: int
+    window_chunks: int
+    max_chunks: int
+    rope_theta: float = 10000.0
+    softmax_scale: float = 0.0
+
+    def to_c(self) -> CkvConfig:
+        return CkvConfig(self.num_layers, self.num_steps, self.num_heads, self.head_dim, self.grid_h,
+                         self.grid_w, self.first_chunk_frames, self.window_chunks, self.max_chunks, 0,
+                         float(self.rope_theta), float(self.softmax_scale), 0)
+
+    @property
+    def frame_tokens(self) -> int:
+        return self.grid_h * self.grid_w
+
+    def tokens(self, chunk: int) -> int:
+        return (self.first_chunk_frames if chunk == 0 else 1) * self.frame_tokens
+
+
+def cache_bytes(cfg: Config) -> int:
+    c = cfg.to_c()
+    return int(load().ckv_cache_bytes(ctypes.byref(c)))
+
+
+def _check(st: int, what: str):
+    if st != CKV_OK:
+        raise CkvError(st, what)
+
+
+class Cache:
+    """One same-step K/V cache (sinks + per-(layer, step) rings) over a torch
+    arena on the current device.  `dry=True` makes a host-only cache that
+    validates and advances the schedule without touching a device; tensor
+    arguments may then be any non-null 16-byte aligned integers."""
+
+    def __init__(self, cfg: Config, dry: bool = False, device=None):
+        self.cfg = cfg
+        self.dry = dry
+        self._lib = load()
+        self._c = cfg.to_c()
+        h = ctypes.c_void_p()
+        if dry:
+            self.arena = None
+            _check(self._lib.ckv_cache_create_dry(ctypes.byref(self._c), ctypes.byref(h)), "ckv_cache_create_dry")
+        else:
+            import torch
+            nbytes = self._lib.ckv_cache_bytes(ctypes.byref(self._c))
+            if nbytes == 0:
+                raise CkvError(CKV_E_INVALID, "ckv_cache_bytes")
+            self.arena = torch.empty(int(nbytes), dtype=torch.uint8, device=device or "cuda")
+            _check(self._lib.ckv_cache_create(ctypes.byref(self._c), self.arena.data_ptr(), int(nbytes),
+                                              ctypes.byref(h)), "ckv_cache_create")
+        self._h = h
+
+    # -- helpers ---------------------------------------------------------
+    def _ptr(self, t, shape, name):
+        if self.dry and isinstance(t, int):
+            return t
+        import torch
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 device tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        return t.data_ptr()
+
+    def _stream(self, stream):
+        if self.dry:
+            return None
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        return s.cuda_stream
+
+    def _shape(self, chunk):
+        return (self.cfg.tokens(chunk), self.cfg.num_heads, self.cfg.head_dim)
+
+    # -- ABI calls ---------------------------------------------------------
+    def rope_append(self, layer, step, chunk, q, k, v, q_rot, stream=None):
+        sh = self._shape(chunk)
+        _check(self._lib.ckv_rope_append(self._h, layer, step, chunk, self._ptr(q, sh, "q"), self._ptr(k, sh, "k"),
+                                         self._ptr(v, sh, "v"), self._ptr(q_rot, sh, "q_rot"),
+                                         self._stream(stream)), "ckv_rope_append")
+
+    def sink_build(self, layer, q, k, v, q_rot, stream=None):
+        sh = self._shape(0)
+        _check(self._lib.ckv_sink_build(self._h, layer, self._ptr(q, sh, "q"), self._ptr(k, sh, "k"),
+                                        self._ptr(v, sh, "v"), self._ptr(q_rot, sh, "q_rot"),
+                                        self._stream(stream)), "ckv_sink_build")
+
+    def chunk_attention(self, layer, step, chunk, q_rot, out, stream=None):
+        sh = self._shape(chunk)
+        _check(self._lib.ckv_chunk_attention(self._h, layer, step, chunk, self._ptr(q_rot, sh, "q_rot"),
+                                             self._ptr(out, sh, "out"), self._stream(stream)),
+               "ckv_chunk_attention")
+
+    def window(self, layer, step, chunk):
+        segs = (CkvSegment * 4)()
+        n = ctypes.c_int32()
+        _check(self._lib.ckv_window(self._h, layer, step, chunk, segs, 4, ctypes.byref(n)), "ckv_window")
+        return [dict(kind=s.kind, first_slot=s.first_slot, chunk_first=s.chunk_first, n_chunks=s.n_chunks,
+                     n_tokens=s.n_tokens) for s in segs[: n.value]]
+
+    def ring_slot(self, chunk):
+        out = ctypes.c_int32()
+        _check(self._lib.ckv_ring_slot(self._h, chunk, ctypes.byref(out)), "ckv_ring_slot")
+        return out.value
+
+    def debug_copy_kv(self, layer, step, chunk, k_out, v_out, stream=None):
+        sh = self._shape(chunk)
+        _check(self._lib.ckv_debug_copy_kv(self._h, layer, step, chunk, self._ptr(k_out, sh, "k_out"),
+                                           self._ptr(v_out, sh, "v_out"), self._stream(stream)),
+               "ckv_debug_copy_kv")
+
+    def attention_splits(self, n_queries, n_keys):
+        return int(self._lib.ckv_attention_splits(self._h, n_queries, n_keys))
+
+    def reset(self):
+        _check(self._lib.ckv_cache_reset(self._h), "ckv_cache_reset")
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.ckv_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

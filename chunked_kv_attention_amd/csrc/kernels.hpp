@@ -1,0 +1,69 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace ckv {
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+
+// Rotate q and k of one chunk by 3D RoPE; write q_rot and the K/V store.
+struct RopeAppendParams {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  bf16_t* q_rot;
+  bf16_t* k_dst;             // [H][rows][d]: the chunk's first row, head 0
+  bf16_t* vt_dst;            // [H][d][cols]: the chunk's first column, head 0
+  long long k_head_stride;   // elements between heads in k_dst
+  long long vt_head_stride;  // elements between heads in vt_dst
+  int vt_row_stride;         // elements between head-dim rows in vt_dst
+  int n_tokens;
+  int num_heads;
+  int first_frame;           // absolute latent frame of the chunk's first frame
+  int grid_h, grid_w;
+  const float* cos_sin;      // [frames][Dt/2] | [grid_h][Dh/2] | [grid_w][Dw/2] float2 (cos, sin)
+  int n_frames_table;
+};
+
+// Up to three runs of keys, in key order; run r holds keys [end[r-1], end[r]).
+struct AttnParams {
+  const bf16_t* q;           // [nq][H][d]
+  bf16_t* out;               // [nq][H][d]
+  const bf16_t* k[3];        // run base, head 0: [rows][d]
+  const bf16_t* vt[3];       // run base, head 0: [d][cols]
+  long long k_head_stride[3];
+  long long vt_head_stride[3];
+  int vt_row_stride[3];
+  int seg_end[3];            // cumulative key counts; unused runs repeat n_keys
+  int n_queries;
+  int n_keys;
+  int num_heads;
+  int n_splits;              // key splits; 1 writes `out` directly
+  int q_tiles;               // ceil(nq / query tile)
+  int key_tiles;             // ceil(n_keys / key tile)
+  float scale_log2;          // softmax scale * log2(e)
+  float* part_o;             // [n_splits][nq][H][d] fp32 (split > 1)
+  float* part_lse;           // [n_splits][nq][H]   log2-domain LSE (split > 1)
+};
+
+struct CopyKVParams {
+  const bf16_t* k_src;  // [H][rows][d] at the chunk's first row
+  const bf16_t* vt_src; // [H][d][cols] at the chunk's first column
+  long long k_head_stride, vt_head_stride;
+  int vt_row_stride;
+  int n_tokens, num_heads;
+  bf16_t* k_out;        // [n][H][d]
+  bf16_t* v_out;        // [n][H][d]
+};
+
+constexpr int kAttnQueryTile = 128;  // query rows per workgroup
+constexpr int kAttnKeyTile = 64;     // keys per LDS tile
+
+hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s);
+hipError_t launch_chunk_attention(const AttnParams& p, int head_dim, hipStream_t s);
+hipError_t launch_copy_kv(const CopyKVParams& p, int head_dim, hipStream_t s);
+
+}  // namespace ckv

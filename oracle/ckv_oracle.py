@@ -32,6 +32,13 @@ notes of the repository):
     column.
   * Softmax scale 1/sqrt(head_dim); no mask inside the window.
   * The sink is stored once per layer and shared by every step.
+  * Attention consumes the rotated q and k in bf16: the rotation itself is
+    float64 ([LG] Ch.4 "3D RoPE" detail paragraph), but the backbone runs in
+    bf16 ([LG] Ch.4, block forward pass) and its attention dependency takes
+    half-precision inputs ([TI] install notes), so the rotated vectors are
+    rounded to bf16 (nearest, ties to even) where they enter attention.
+    Everything after that (scores, softmax, weighted sum) is float64.
+    `OracleConfig.attention_inputs = "f64"` keeps them unrounded.
 """
 
 from __future__ import annotations
@@ -151,6 +158,14 @@ def rope3d(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
     return out
 
 
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits, ties to even) of float64 values,
+    returned as float64.  Finite inputs in the normal bf16 range."""
+    x = np.asarray(x, dtype=np.float64)
+    mant, expo = np.frexp(x)                  # x = mant * 2^expo, 0.5 <= |mant| < 1
+    return np.ldexp(np.rint(np.ldexp(mant, 8)), expo - 8)
+
+
 # --------------------------------------------------------------------------
 # Window membership ([MC] "Inference profile": up to W recent chunks plus the
 # first-chunk sink without duplication; same-step reads)
@@ -190,13 +205,15 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndar
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     nq, nh, d = q.shape
+    kh = np.ascontiguousarray(k.transpose(1, 0, 2))      # [H, nk, d]
+    vh = np.ascontiguousarray(v.transpose(1, 0, 2))
     out = np.empty((nq, nh, v.shape[2]), dtype=np.float64)
     for h in range(nh):
-        z = scale * (q[:, h, :] @ k[:, h, :].T)          # [nq, nk]
+        z = scale * (q[:, h, :] @ kh[h].T)               # [nq, nk]
         m = z.max(axis=1, keepdims=True)
         p = np.exp(z - m)
         p /= p.sum(axis=1, keepdims=True)
-        out[:, h, :] = p @ v[:, h, :]
+        out[:, h, :] = p @ vh[h]
     return out
 
 
@@ -219,6 +236,7 @@ class OracleConfig:
     max_chunks: int
     rope_theta: float = 10000.0
     softmax_scale: float = 0.0
+    attention_inputs: str = "bf16"   # precision rotated q/k enter attention in
 
     @property
     def scale(self) -> float:
@@ -243,7 +261,9 @@ class OracleRollout:
     noisy: dict = field(default_factory=dict)
 
     def rotate(self, chunk: int, x) -> np.ndarray:
-        return rope3d(x, self.cfg.positions(chunk), self.cfg.rope_theta)
+        """RoPE in float64, then the hand-off precision of attention's inputs."""
+        r = rope3d(x, self.cfg.positions(chunk), self.cfg.rope_theta)
+        return round_to_bf16(r) if self.cfg.attention_inputs == "bf16" else r
 
     def first_chunk_step(self, layer, step, q, k, v, rows=None):
         """Chunk 0, noisy step: self-attention within the chunk only."""

@@ -1,0 +1,177 @@
+"""Helpers for the GPU parity tests: device transfer of bf16 bit patterns, the
+comparison metrics, and a driver that runs the same seeded rollout through the
+C-ABI and through the oracle."""
+
+from __future__ import annotations
+
+import dataclasses
+import zlib
+
+import numpy as np
+import torch
+
+import chunked_kv_attention_amd as C
+import oracle.ckv_oracle as O
+from chunked_kv_attention_amd import inputs as I
+
+MAX_ABS = 2e-2   # attention output, bf16 inputs, against the float64 oracle
+REL_L2 = 5e-3
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU test needs a HIP device"
+    C.load()  # raises if libckv.so was not built
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 of a bf16 device tensor."""
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return I.bf16_bits_to_f64(bits)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 round-to-nearest-even, directly from float64."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                   # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)  # 8 significant bits, ties to even
+    return I.f32_to_bf16_bits(q.astype(np.float32))
+
+
+def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in bf16 ulps between two bf16 bit arrays (finite values)."""
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def attn_errors(got: np.ndarray, ref: np.ndarray):
+    diff = got - ref
+    return float(np.abs(diff).max()), float(np.linalg.norm(diff) / np.linalg.norm(ref))
+
+
+def assert_attn_close(got, ref, what=""):
+    mx, rl2 = attn_errors(got, ref)
+    assert np.isfinite(got).all(), what
+    assert mx <= MAX_ABS and rl2 <= REL_L2, f"{what}: max abs {mx:.3e}, rel L2 {rl2:.3e}"
+    return mx, rl2
+
+
+def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
+    """Rows spread over every query tile, always including the first and the
+    last row and the tile edges near the end."""
+    rng = np.random.default_rng(seed)
+    fixed = {0, n - 1, min(n - 1, 127), min(n - 1, 128), max(0, (n // 128) * 128 - 1), max(0, n - 17)}
+    rest = rng.choice(n, size=min(n, count), replace=False)
+    return np.array(sorted(fixed | set(int(r) for r in rest)))
+
+
+class Rollout:
+    """Runs chunks through one cache on the GPU and through the oracle, on the
+    same seeded bf16 inputs, and compares each attention output (all rows, or
+    a sample of rows when `rows_per_call` is set)."""
+
+    def __init__(self, cfg: C.Config, base_seed=0, prompt=0, rows_per_call=None, stream=None, also_f64=False):
+        self.cfg = cfg
+        self.cache = C.Cache(cfg)
+        self.ocfg = O.OracleConfig(cfg.num_layers, cfg.num_steps, cfg.num_heads, cfg.head_dim, cfg.grid_h,
+                                   cfg.grid_w, cfg.first_chunk_frames, cfg.window_chunks, cfg.max_chunks,
+                                   cfg.rope_theta, cfg.softmax_scale)
+        self.oracle = O.OracleRollout(self.ocfg)
+        # optional second oracle that keeps rotated q/k unrounded (reported, not asserted)
+        self.oracle64 = O.OracleRollout(dataclasses.replace(self.ocfg, attention_inputs="f64")) if also_f64 else None
+        self.worst64 = (0.0, 0.0)
+        self.seed = base_seed
+        self.prompt = prompt
+        self.rows_per_call = rows_per_call
+        self.stream = stream
+        self.worst = (0.0, 0.0)
+
+    def inputs(self, layer, chunk, step_code, scale_rows=None):
+        n = self.cfg.tokens(chunk)
+        shape = (n, self.cfg.num_heads, self.cfg.head_dim)
+        key = dict(base_seed=self.seed, prompt=self.prompt, layer=layer, chunk=chunk, step_code=step_code)
+        q = I.draw(shape, tensor="q", **key)
+        k = I.draw(shape, tensor="k", **key)
+        v = I.draw(shape, tensor="v", **key)
+        if scale_rows is not None and len(scale_rows):
+            k[scale_rows] *= 4.0
+        return tuple(I.f32_to_bf16_bits(x) for x in (q, k, v))
+
+    def _rows(self, n, tag):
+        if self.rows_per_call is None or self.rows_per_call >= n:
+            return None
+        return sample_rows(n, self.rows_per_call, seed=zlib.crc32(repr(tag).encode()))
+
+    def _run(self, kind, layer, step, chunk, bits):
+        q, k, v = (to_dev(b) for b in bits)
+        qr = torch.empty_like(q)
+        out = torch.empty_like(q)
+        s = self.stream
+        if kind == "sink":
+            self.cache.sink_build(layer, q, k, v, qr, stream=s)
+            self.cache.chunk_attention(layer, C.STEP_SINK, 0, qr, out, stream=s)
+        else:
+            self.cache.rope_append(layer, step, chunk, q, k, v, qr, stream=s)
+            self.cache.chunk_attention(layer, step, chunk, qr, out, stream=s)
+        return qr, out
+
+    def step(self, kind, layer, step, chunk, scale_rows=None, check=True):
+        """kind: 'first' (chunk 0 noisy step), 'sink' (clean pass), 'chunk'."""
+        step_code = self.cfg.num_steps if kind == "sink" else step
+        bits = self.inputs(layer, chunk, step_code, scale_rows)
+        qr_dev, out_dev = self._run(kind, layer, step, chunk, bits)
+        if self.stream is not None:
+            self.stream.synchronize()  # inputs were allocated on the current stream
+        q, k, v = (I.bf16_bits_to_f64(b) for b in bits)
+        # unchecked calls only record K/V in the oracle: attend one row
+        rows = self._rows(q.shape[0], (layer, step, chunk, kind)) if check else np.array([0])
+        refs = []
+        for orc in (self.oracle, self.oracle64):
+            if orc is None:
+                continue
+            if kind == "first":
+                ref, _ = orc.first_chunk_step(layer, step, q, k, v, rows=rows)
+            elif kind == "sink":
+                ref, _ = orc.sink_pass(layer, q, k, v, rows=rows)
+            else:
+                ref, _ = orc.chunk_step(layer, step, chunk, q, k, v, rows=rows)
+            refs.append(ref)
+        if not check:
+            return None
+        ref = refs[0]
+        got = from_dev(out_dev)
+        if rows is not None:
+            got = got[rows]
+        if self.oracle64 is not None:
+            e64 = attn_errors(got, refs[1])
+            self.worst64 = (max(self.worst64[0], e64[0]), max(self.worst64[1], e64[1]))
+        errs = assert_attn_close(got, ref, f"{kind} layer {layer} step {step} chunk {chunk}")
+        self.worst = (max(self.worst[0], errs[0]), max(self.worst[1], errs[1]))
+        return errs
+
+    def run_first_chunk(self, layers=None):
+        layers = range(self.cfg.num_layers) if layers is None else layers
+        for s in range(self.cfg.num_steps):
+            for layer in layers:
+                self.step("first", layer, s, 0)
+        for layer in layers:
+            self.step("sink", layer, 0, 0)
+
+    def run_chunks(self, chunks, layers=None, steps=None, progress=False):
+        layers = range(self.cfg.num_layers) if layers is None else layers
+        steps = range(self.cfg.num_steps) if steps is None else steps
+        for c in chunks:
+            for s in steps:
+                for layer in layers:
+                    self.step("chunk", layer, s, c)
+            if progress:
+                print(f"  chunk {c} ok (worst max abs {self.worst[0]:.2e}, rel L2 {self.worst[1]:.2e})", flush=True)

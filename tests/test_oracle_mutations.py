@@ -84,6 +84,18 @@ def _flops_one_matmul(lq, lk, width):
     return 2 * lq * lk * width
 
 
+def _round_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
+
+
+def _round_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.sign(m) * np.floor(np.abs(np.ldexp(m, 8)) + 0.5), e - 8)
+
+
 _ORIG_ATTEND = O.attend
 
 MUTATIONS = [
@@ -98,6 +110,8 @@ MUTATIONS = [
     ("window_chunks", _window_off_by_one, [lambda: P.test_window_matches_fifo_simulation(2), P.test_window_golden]),
     ("token_positions", _tokens_transposed, [P.test_token_positions_brute_force]),
     ("attention_flops", _flops_one_matmul, [P.test_flop_formula_worked_example]),
+    ("round_to_bf16", _round_truncate, [P.test_round_to_bf16_ties_and_library]),
+    ("round_to_bf16", _round_ties_away, [P.test_round_to_bf16_ties_and_library]),
 ]
 
 

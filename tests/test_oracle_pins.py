@@ -265,14 +265,44 @@ def test_rollout_chunk_step_matches_direct_definition():
     ro = O.OracleRollout(cfg)
     q0, k0, v0 = _rand(24, 2, 64), _rand(24, 2, 64), _rand(24, 2, 64)
     ro.sink_pass(0, q0, k0, v0)
-    ks, vs = [O.rope3d(k0, cfg.positions(0), 1e4)], [v0]
+    bf = O.round_to_bf16
+    ks, vs = [bf(O.rope3d(k0, cfg.positions(0), 1e4))], [v0]
     for c in range(1, 5):
         q, k, v = _rand(8, 2, 64), _rand(8, 2, 64), _rand(8, 2, 64)
         o, _ = ro.chunk_step(0, 0, c, q, k, v)
-        kr = O.rope3d(k, cfg.positions(c), 1e4)
+        kr = bf(O.rope3d(k, cfg.positions(c), 1e4))
         win_k = [ks[0]] + [ks[j] for j in O.window_chunks(c, 2)] + [kr]
         win_v = [vs[0]] + [vs[j] for j in O.window_chunks(c, 2)] + [v]
-        ref = O.attend(O.rope3d(q, cfg.positions(c), 1e4), np.concatenate(win_k), np.concatenate(win_v), 0.125)
+        ref = O.attend(bf(O.rope3d(q, cfg.positions(c), 1e4)), np.concatenate(win_k), np.concatenate(win_v), 0.125)
         np.testing.assert_allclose(o, ref, atol=1e-13)
         ks.append(kr)
         vs.append(v)
+
+
+# -------------------------------------------------------- bf16 hand-off --
+
+def test_round_to_bf16_ties_and_library():
+    """Ties go to the even significand; agrees with torch's float32 -> bfloat16
+    conversion (round-to-nearest-even) on float32-representable values."""
+    one = 1.0
+    assert O.round_to_bf16(np.array([one + 2.0 ** -8]))[0] == 1.0                     # tie -> even
+    assert O.round_to_bf16(np.array([one + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6      # tie -> even (up)
+    assert O.round_to_bf16(np.array([one + 2.0 ** -8 + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+    assert O.round_to_bf16(np.array([-(one + 2.0 ** -8)]))[0] == -1.0
+    x = RNG.standard_normal(20000).astype(np.float32) * np.float32(37.0)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_bf16(x.astype(np.float64)), ref)
+
+
+def test_rollout_rounds_rotated_qk_only():
+    """The rollout hands bf16-rounded rotated q/k to attention; V untouched."""
+    cfg = O.OracleConfig(1, 1, 2, 64, 2, 4, 3, 2, 5)
+    ro = O.OracleRollout(cfg)
+    q, k, v = _rand(24, 2, 64), _rand(24, 2, 64), _rand(24, 2, 64)
+    _, (qr, kr) = ro.sink_pass(0, q, k, v)
+    full = O.rope3d(k, cfg.positions(0), 1e4)
+    np.testing.assert_array_equal(kr, O.round_to_bf16(full))
+    np.testing.assert_array_equal(ro.sink[0][1], v)
+    cfg64 = O.OracleConfig(1, 1, 2, 64, 2, 4, 3, 2, 5, attention_inputs="f64")
+    _, (_, kr64) = O.OracleRollout(cfg64).sink_pass(0, q, k, v)
+    np.testing.assert_array_equal(kr64, full)
