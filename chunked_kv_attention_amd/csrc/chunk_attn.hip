@@ -5,22 +5,37 @@
 // profile"): for every head and query, softmax(scale * q K_win^T) V_win over
 // the window [sink | same-step ring window | own chunk], no mask.  The
 // window is not concatenated: it arrives as up to three runs of keys (the
-// sink, then up to two runs of ring slots) and every 8-key group of a tile is
-// addressed in the run that holds it.
+// sink, then up to two runs of ring slots) and every 16-byte piece of a tile
+// is fetched from the run that holds it.
 //
 // Tiling.  A workgroup is 4 waves; each wave owns 32 query rows of one head
 // (128 rows per workgroup).  Keys stream through LDS in tiles of 64: K rows
-// [64][d] and V^T [d][64], padded so that the 16-byte MFMA operand reads are
-// bank-conflict free.  Per tile and wave:
-//   S^T[64 keys x 32 queries] = K_tile Q^T   (v_mfma_f32_32x32x16_bf16)
-// with the queries as the MFMA's N columns, so one lane holds 32 scores of a
-// single query and the row max / row sum need only one cross-half exchange
-// (v_permlane32_swap).  The K rows feeding the A operand are permuted
-// (bits 2 and 3 of the row swapped) so that the 8 scores a lane holds for
-// each 16-key step of the next product are 8 consecutive keys:
-//   O^T[d x 32 queries] += V^T_tile P^T       (v_mfma_f32_32x32x16_bf16)
-// takes P straight from registers (converted to bf16) and V^T from LDS with
-// one 16-byte read per lane.
+// [64][d] and V^T [d][64], each row padded by 16 bytes.  Tiles are fetched
+// straight into LDS (global_load_lds_dwordx4, no staging registers): each
+// lane is given the global 16-byte piece that belongs at its LDS position,
+// so padding and row order cost nothing.  Two LDS buffers alternate; tile
+// t+1 is in flight while tile t is computed, with one barrier per tile.
+//
+// Products use v_mfma_f32_16x16x32_bf16 (16x16 output blocks): per tile and
+// wave
+//   S^T[64 keys x 32 queries] = K_tile Q^T      8 independent 16x16 blocks
+//   O^T[d x 32 queries]      += V^T_tile P^T    2d/16 independent blocks
+// so both products keep many accumulation chains in flight.  With the
+// queries as the N columns, a lane holds 16 scores of each of its 2 queries;
+// a query's row max needs a 4-lane exchange (lane xor 16, xor 32).  K rows
+// sit in LDS in a permuted order chosen so that (a) the 16 rows one MFMA
+// reads are consecutive LDS rows (conflict-free, immediate offsets) and (b)
+// the 8 scores a lane holds for each 32-key step of the PV product are 8
+// consecutive keys, so P goes from registers straight into the B operand and
+// V^T needs one 16-byte LDS read per lane.
+//
+// Softmax.  Scores stay raw; the scale (times log2 e) is folded into one FMA
+// per score before exp2.  The running max is lazy: O and the running sum are
+// rescaled only when a tile raises some row's max by more than 2^8 (a
+// wave-uniform branch), otherwise the stale max is kept and P may reach 256,
+// which bf16 and the fp32 accumulators hold exactly enough.  The running sum
+// adds the bf16-rounded P with v_dot2_f32_bf16, so numerator and denominator
+// see the same weights.
 //
 // Occupancy.  880 queries x 24 heads is only 168 workgroups of 128 rows for
 // 256 CUs, so the key range is split into up to 4 parts when that fills the
@@ -40,96 +55,301 @@ namespace ckv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int QT = kAttnQueryTile;  // 128
 constexpr int KT = kAttnKeyTile;    // 64
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr int KB = KT / 16;           // 16-key blocks of S^T per tile
+constexpr int KS = KT / 32;           // 32-key steps of the PV product per tile
 
 template <int D>
-struct Smem {
-  uint16_t k[KT][D + 8];   // key rows, padded by 16 bytes
-  uint16_t vt[D][KT + 8];  // head-dim rows of V^T, padded by 16 bytes
+struct Tile {
+  static constexpr int kRowK = D + 8;               // bf16 per padded K row
+  static constexpr int kRowV = KT + 8;              // bf16 per padded V^T row
+  static constexpr int kChK = kRowK / 8;            // 16-byte pieces per K row (last one is padding)
+  static constexpr int kChV = kRowV / 8;
+  static constexpr int kPiecesK = KT * kChK;
+  static constexpr int kPiecesV = D * kChV;
+  static constexpr int kBlocksK = kPiecesK / 64;    // 1 KB blocks, one wave instruction each
+  static constexpr int kBlocksV = kPiecesV / 64;
+  static constexpr int kSlotsK = (kBlocksK + kWaves - 1) / kWaves;
+  static constexpr int kSlotsV = (kBlocksV + kWaves - 1) / kWaves;
+  static_assert(kPiecesK % 64 == 0 && kPiecesV % 64 == 0, "LDS tiles must be whole 1 KB blocks");
 };
+
+// K rows sit in LDS in a permuted order: LDS row p = 32s + 16b + 4h + i holds
+// tile key 32s + 8h + 4b + i.  MFMA block kb = 2s + b then reads LDS rows
+// 16kb .. 16kb+15, and the lane group h gets keys 32s + 8h + 4b + (0..3).
+__device__ inline int key_of_lds_row(int p) { return (p & ~31) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3); }
 
 __device__ inline bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
-__device__ inline float pair_max(float x) {
+// max / sum over the 4 lanes l, l^16, l^32, l^48 that share a query
+__device__ inline float quad_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
-__device__ inline float pair_sum(float x) {
+__device__ inline float quad_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-// Run holding key j (runs are ordered and end at seg_end[0..2]).
-__device__ inline int run_of(const AttnParams& p, int j) { return (j >= p.seg_end[0]) + (j >= p.seg_end[1]); }
+// The up to three runs of this head's window, loaded once into uniform
+// scalars (no indexed access to the parameter block, which would force a
+// private-memory copy of it).
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline const char* uni(const void* ptr) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(ptr);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+}
 
+struct Runs {
+  const char *k0, *k1, *k2;  // this head's K row of each run's first key
+  const char *v0, *v1, *v2;  // this head's V^T column of each run's first key
+  int vrs0, vrs1, vrs2;      // V^T row strides (elements)
+  int e0, e1, e2;            // cumulative key ends of the runs
+};
+
+__device__ inline Runs load_runs(const AttnParams& p, int head) {
+  Runs R;
+  R.k0 = uni(p.k[0] + head * p.k_head_stride[0]);
+  R.k1 = uni(p.k[1] + head * p.k_head_stride[1]);
+  R.k2 = uni(p.k[2] + head * p.k_head_stride[2]);
+  R.v0 = uni(p.vt[0] + head * p.vt_head_stride[0]);
+  R.v1 = uni(p.vt[1] + head * p.vt_head_stride[1]);
+  R.v2 = uni(p.vt[2] + head * p.vt_head_stride[2]);
+  R.vrs0 = uni(p.vt_row_stride[0]);
+  R.vrs1 = uni(p.vt_row_stride[1]);
+  R.vrs2 = uni(p.vt_row_stride[2]);
+  R.e0 = uni(p.seg_end[0]);
+  R.e1 = uni(p.seg_end[1]);
+  R.e2 = uni(p.seg_end[2]);
+  return R;
+}
+
+// Which LDS pieces this lane fetches: for slot i, block wave + 4i of the K
+// (or V^T) tile, piece lane of that block.
 template <int D>
-__device__ inline const uint16_t* key_row(const AttnParams& p, int head, int j) {
-  const int r = run_of(p, j);
-  const int start = r == 0 ? 0 : (r == 1 ? p.seg_end[0] : p.seg_end[1]);
-  const uint16_t* base = r == 0 ? p.k[0] : (r == 1 ? p.k[1] : p.k[2]);
-  const long long hs = r == 0 ? p.k_head_stride[0] : (r == 1 ? p.k_head_stride[1] : p.k_head_stride[2]);
-  return base + head * hs + (long long)(j - start) * D;
-}
-
-__device__ inline const uint16_t* vt_col(const AttnParams& p, int head, int dim, int j) {
-  const int r = run_of(p, j);
-  const int start = r == 0 ? 0 : (r == 1 ? p.seg_end[0] : p.seg_end[1]);
-  const uint16_t* base = r == 0 ? p.vt[0] : (r == 1 ? p.vt[1] : p.vt[2]);
-  const long long hs = r == 0 ? p.vt_head_stride[0] : (r == 1 ? p.vt_head_stride[1] : p.vt_head_stride[2]);
-  const int rs = r == 0 ? p.vt_row_stride[0] : (r == 1 ? p.vt_row_stride[1] : p.vt_row_stride[2]);
-  return base + head * hs + (long long)dim * rs + (j - start);
-}
-
-template <int D>
-struct TileRegs {
-  static constexpr int kK = KT * (D / 8) / kThreads;  // 16-byte K chunks per thread
-  static constexpr int kV = D * (KT / 8) / kThreads;  // 16-byte V^T chunks per thread
-  uint4 k[kK];
-  uint4 v[kV];
+struct LaneSlots {
+  int k_key[Tile<D>::kSlotsK];  // tile key whose row this piece belongs to
+  int k_off[Tile<D>::kSlotsK];  // byte offset of the piece in the tile's key rows (key*D + 8*chunk)*2
+  int v_dim[Tile<D>::kSlotsV];  // head-dim row of V^T
+  int v_key[Tile<D>::kSlotsV];  // first of the piece's 8 keys in the tile
+  int v_off[Tile<D>::kSlotsV];  // byte offset in the current run: (v_dim*row_stride + v_key)*2
 };
 
 template <int D>
-__device__ inline void load_tile(const AttnParams& p, int head, int t0, int key_end, TileRegs<D>& r) {
+__device__ inline void make_slots(LaneSlots<D>& s, int wave, int lane) {
+  using T = Tile<D>;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kK; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    const int row = idx / (D / 8), c = idx % (D / 8);
-    const int j = t0 + row;
-    r.k[i] = j < key_end ? *reinterpret_cast<const uint4*>(key_row<D>(p, head, j) + c * 8) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < T::kSlotsK; ++i) {
+    const int piece = (wave + kWaves * i) * 64 + lane;
+    const int row = piece / T::kChK;
+    int ch = piece % T::kChK;
+    if (ch == T::kChK - 1) ch = 0;  // padding piece: fetch something valid, never read
+    s.k_key[i] = row < KT ? key_of_lds_row(row) : 0;
+    s.k_off[i] = (s.k_key[i] * D + 8 * ch) * 2;
   }
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kV; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    const int dim = idx / (KT / 8), g = idx % (KT / 8);
-    const int j = t0 + 8 * g;  // runs are multiples of 8 keys: a group never straddles two runs
-    r.v[i] = j < key_end ? *reinterpret_cast<const uint4*>(vt_col(p, head, dim, j)) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < T::kSlotsV; ++i) {
+    const int piece = (wave + kWaves * i) * 64 + lane;
+    const int dim = piece / T::kChV;
+    int ch = piece % T::kChV;
+    if (ch == T::kChV - 1) ch = 0;
+    s.v_dim[i] = dim < D ? dim : 0;
+    s.v_key[i] = 8 * ch;
+    s.v_off[i] = 0;
   }
 }
 
+// Sequential walk over this workgroup's keys.  The run (sink area or a run
+// of ring slots) holding the next tile changes at most twice per workgroup;
+// within a run a tile's source is a uniform base plus fixed per-lane offsets.
+// Runs are chosen by comparing key boundaries, never by an index (an index
+// would turn the choice into a table in private memory).
+struct RunCursor {
+  int begin, end;  // key range of the current run
+  const char* k;   // K row of key `begin`
+  const char* vt;  // V^T column of key `begin`
+};
+
 template <int D>
-__device__ inline void store_tile(Smem<D>& sm, const TileRegs<D>& r) {
+__device__ inline void cursor_set(RunCursor& c, LaneSlots<D>& s, int begin, int end, const char* k, const char* vt,
+                                  int vrs) {
+  c.begin = begin;
+  c.end = end;
+  c.k = k;
+  c.vt = vt;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kK; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    *reinterpret_cast<uint4*>(&sm.k[idx / (D / 8)][(idx % (D / 8)) * 8]) = r.k[i];
-  }
+  for (int i = 0; i < Tile<D>::kSlotsV; ++i) s.v_off[i] = (s.v_dim[i] * vrs + s.v_key[i]) * 2;
+}
+
+// Place the cursor on the run holding key j (uniform j).
+template <int D>
+__device__ inline void cursor_seek(const Runs& R, RunCursor& c, LaneSlots<D>& s, int j) {
+  if (j < R.e0)
+    cursor_set<D>(c, s, 0, R.e0, R.k0, R.v0, R.vrs0);
+  else if (j < R.e1)
+    cursor_set<D>(c, s, R.e0, R.e1, R.k1, R.v1, R.vrs1);
+  else
+    cursor_set<D>(c, s, R.e1, R.e2, R.k2, R.v2, R.vrs2);
+}
+
+// Source of key j's K row / of V^T row `dim` at key j, for per-lane j.
+template <int D>
+__device__ inline const char* k_row_of(const Runs& R, int j) {
+  return j < R.e0 ? R.k0 + (long long)j * (2 * D)
+                  : (j < R.e1 ? R.k1 + (long long)(j - R.e0) * (2 * D) : R.k2 + (long long)(j - R.e1) * (2 * D));
+}
+__device__ inline const char* vt_at(const Runs& R, int dim, int j) {
+  return j < R.e0 ? R.v0 + ((long long)dim * R.vrs0 + j) * 2
+                  : (j < R.e1 ? R.v1 + ((long long)dim * R.vrs1 + (j - R.e0)) * 2
+                              : R.v2 + ((long long)dim * R.vrs2 + (j - R.e1)) * 2);
+}
+
+// Enqueue the fetch of key tile [t0, t0 + KT) into one LDS buffer pair.
+template <int D>
+__device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, int wave, int t0, int key_begin,
+                                  int key_end, uint4* sk, uint4* sv) {
+  using T = Tile<D>;
+  if (t0 >= c.end) cursor_seek<D>(R, c, s, t0);
+  if (t0 + KT <= c.end && t0 + KT <= key_end) {
+    const char* kb = c.k + (long long)(t0 - c.begin) * (2 * D);
+    const char* vb = c.vt + (long long)(t0 - c.begin) * 2;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kV; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    *reinterpret_cast<uint4*>(&sm.vt[idx / (KT / 8)][(idx % (KT / 8)) * 8]) = r.v[i];
+    for (int i = 0; i < T::kSlotsK; ++i)
+      if (i < T::kBlocksK / kWaves || wave + kWaves * i < T::kBlocksK)
+        __builtin_amdgcn_global_load_lds(kb + s.k_off[i], (lds_void*)(sk + (wave + kWaves * i) * 64), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < T::kSlotsV; ++i)
+      if (i < T::kBlocksV / kWaves || wave + kWaves * i < T::kBlocksV)
+        __builtin_amdgcn_global_load_lds(vb + s.v_off[i], (lds_void*)(sv + (wave + kWaves * i) * 64), 16, 0, 0);
+  } else {
+    // Tile straddles two runs or the end of this split's keys: per-lane
+    // lookup; keys past the end fetch key_begin (finite data; masked later).
+#pragma unroll
+    for (int i = 0; i < T::kSlotsK; ++i)
+      if (i < T::kBlocksK / kWaves || wave + kWaves * i < T::kBlocksK) {
+        int j = t0 + s.k_key[i];
+        if (j >= key_end) j = key_begin;
+        __builtin_amdgcn_global_load_lds(k_row_of<D>(R, j) + (s.k_off[i] - s.k_key[i] * 2 * D),
+                                         (lds_void*)(sk + (wave + kWaves * i) * 64), 16, 0, 0);
+      }
+#pragma unroll
+    for (int i = 0; i < T::kSlotsV; ++i)
+      if (i < T::kBlocksV / kWaves || wave + kWaves * i < T::kBlocksV) {
+        int j = t0 + s.v_key[i];  // runs are multiples of 8 keys: a piece never straddles two runs
+        if (j >= key_end) j = key_begin;
+        __builtin_amdgcn_global_load_lds(vt_at(R, s.v_dim[i], j), (lds_void*)(sv + (wave + kWaves * i) * 64), 16,
+                                         0, 0);
+      }
   }
+}
+
+// One key tile for a wave's 32 queries (2 blocks of 16):
+//   S^T = K_tile Q^T, online softmax per query, O^T += V^T_tile P^T.
+// S value (kb, qb)[i] is the score of tile key 32s + 8h + 4b + i (kb = 2s + b,
+// h = lane / 16) for query 16qb + lane % 16.  O value (db, qb)[i] is head dim
+// 16db + 4h + i of that query.
+template <int D>
+__device__ inline void attend_tile(const char* kbase, const char* vbase, const bf16x8 (&qf)[D / 32][2],
+                                   f32x4 (&o)[D / 16][2], float (&m)[2], float (&lsum)[2], float scale_log2,
+                                   bool masked, int t0, int key_end, int h) {
+  using T = Tile<D>;
+  constexpr int KK = D / 32;
+  constexpr int DB = D / 16;
+  f32x4 s[KB][2];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + (16 * kb * T::kRowK + 32 * kk) * 2));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk][qb], s[kb][qb], 0, 0, 0);
+    }
+
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 32 * (kb / 2) + 8 * h + 4 * (kb % 2) + i >= key_end) s[kb][qb][i] = -INFINITY;
+  }
+  float mt[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = s[0][qb][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+    mt[qb] = quad_max(mx) * scale_log2;
+  }
+  if (__any(mt[0] > m[0] + kRescaleLog2 || mt[1] > m[1] + kRescaleLog2)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_new = fmaxf(m[qb], mt[qb]);
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
+      lsum[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
+      m[qb] = m_new;
+    }
+  }
+
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 pf[KS][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float neg_m = -m[qb];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], scale_log2, neg_m));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i + 1], scale_log2, neg_m));
+        const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+        lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum[qb], false);
+        pf[kb / 2][qb][4 * (kb % 2) + i] = pk[0];
+        pf[kb / 2][qb][4 * (kb % 2) + i + 1] = pk[1];
+      }
+  }
+
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(vbase + (16 * db * T::kRowV + 32 * ks) * 2));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[ks][qb], o[db][qb], 0, 0, 0);
+    }
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
-  constexpr int KK = D / 16;  // 16-deep steps of the QK^T product
-  constexpr int MO = D / 32;  // 32-row head-dim blocks of O^T
-  __shared__ Smem<D> sm;
+  using T = Tile<D>;
+  constexpr int KK = D / 32;
+  constexpr int DB = D / 16;
+  __shared__ uint4 sk0[T::kPiecesK], sk1[T::kPiecesK];
+  __shared__ uint4 sv0[T::kPiecesV], sv1[T::kPiecesV];
 
   // Work unit: contiguous runs of (head, split, q-tile) per XCD.
   const int units = p.q_tiles * p.num_heads * p.n_splits;
@@ -145,124 +365,81 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
   const int key_end = min((int)((long long)p.key_tiles * (split + 1) / p.n_splits) * KT, p.n_keys);
   const int t_begin = key_begin / KT, t_end = (key_end + KT - 1) / KT;
 
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int half = lane / 32, col = lane % 32;
-  const int q_row = qt * QT + wave * 32 + col;
-  const bool q_valid = q_row < p.n_queries;
-  // A-operand row -> key row of the tile: swap bits 2 and 3.
-  const int prow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+  // wave index as a scalar: block choices and LDS-DMA bases depend on it
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
+  const int h = lane / 16, c16 = lane % 16;
+  const int k_lane_byte = (c16 * T::kRowK + 8 * h) * 2;
+  const int v_lane_byte = (c16 * T::kRowV + 8 * h) * 2;
 
-  bf16x8 qf[KK];
-  {
-    const uint16_t* qp = p.q + ((long long)(q_valid ? q_row : 0) * p.num_heads + head) * D + 8 * half;
+  LaneSlots<D> slots;
+  make_slots<D>(slots, wave, lane);
+  const Runs runs = load_runs(p, head);
+  RunCursor cursor;
+  cursor_seek<D>(runs, cursor, slots, key_begin);
+
+  // Q^T B operand: lane holds head dims 32kk + 8h .. +8 of query 16qb + c16.
+  bf16x8 qf[KK][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q_row = qt * QT + wave * 32 + 16 * qb + c16;
+    const bool ok = q_row < p.n_queries;
+    const uint16_t* qp = p.q + ((long long)(ok ? q_row : 0) * p.num_heads + head) * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = as_bf16x8(q_valid ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0));
+      qf[kk][qb] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0));
   }
 
-  f32x16 o[MO];
+  f32x4 o[DB][2];
 #pragma unroll
-  for (int mo = 0; mo < MO; ++mo)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[mo][i] = 0.f;
-  float m = -INFINITY;  // running max of scaled scores (log2 domain), same in both halves
-  float lsum = 0.f;     // this lane's share of the running sum
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};  // running max of scaled scores (log2 domain), per query block
+  float lsum[2] = {0.f, 0.f};           // this lane's share of the running sums
 
-  TileRegs<D> regs;
-  load_tile<D>(p, head, t_begin * KT, key_end, regs);
-  store_tile<D>(sm, regs);
-  __syncthreads();
+  const char* kl0 = reinterpret_cast<const char*>(sk0) + k_lane_byte;
+  const char* kl1 = reinterpret_cast<const char*>(sk1) + k_lane_byte;
+  const char* vl0 = reinterpret_cast<const char*>(sv0) + v_lane_byte;
+  const char* vl1 = reinterpret_cast<const char*>(sv1) + v_lane_byte;
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int t0 = t * KT;
-    if (t + 1 < t_end) load_tile<D>(p, head, t0 + KT, key_end, regs);
-
-    f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[32 * mb + prow][16 * kk + 8 * half]));
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
-      }
-
-    // Lane value (mb, i) is the score of tile key 32mb + 16(i/8) + 8*half + i%8.
-    float mloc = -INFINITY;
-    const bool tail = t0 + KT > key_end;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[mb][i] * p.scale_log2;
-        if (tail && t0 + 32 * mb + 16 * (i / 8) + 8 * half + (i % 8) >= key_end) x = -INFINITY;
-        s[mb][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    const float m_new = fmaxf(m, pair_max(mloc));
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    float psum = 0.f;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(s[mb][i] - m_new);
-        psum += e;
-        pf[2 * mb + i / 8][i % 8] = (__bf16)e;
-      }
-    lsum = lsum * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int mo = 0; mo < MO; ++mo)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[mo][i] *= alpha;
-
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int mo = 0; mo < MO; ++mo) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.vt[32 * mo + col][16 * kb + 8 * half]));
-        o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb], o[mo], 0, 0, 0);
-      }
-
+  fetch_tile<D>(runs, slots, cursor, wave, t_begin * KT, key_begin, key_end, sk0, sv0);
+  for (int t = t_begin; t < t_end; t += 2) {
+    // buffer 0 holds tile t; tile t+1 goes to buffer 1 while t is computed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < t_end) store_tile<D>(sm, regs);
+    if (t + 1 < t_end) fetch_tile<D>(runs, slots, cursor, wave, (t + 1) * KT, key_begin, key_end, sk1, sv1);
+    attend_tile<D>(kl0, vl0, qf, o, m, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
+    if (t + 1 >= t_end) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (t + 2 < t_end) fetch_tile<D>(runs, slots, cursor, wave, (t + 2) * KT, key_begin, key_end, sk0, sv0);
+    attend_tile<D>(kl1, vl1, qf, o, m, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT, key_end, h);
   }
 
-  const float ltot = pair_sum(lsum);
-  const float inv = 1.f / ltot;
-  if (!q_valid) return;
-  // O^T value (mo, i) is head-dim 32mo + 8(i/4) + 4*half + i%4 of query q_row.
-  if (p.n_splits == 1) {
-    uint16_t* op = p.out + ((long long)q_row * p.num_heads + head) * D + 4 * half;
 #pragma unroll
-    for (int mo = 0; mo < MO; ++mo)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q_row = qt * QT + wave * 32 + 16 * qb + c16;
+    const float ltot = quad_sum(lsum[qb]);
+    const float inv = 1.f / ltot;
+    if (q_row >= p.n_queries) continue;
+    if (p.n_splits == 1) {
+      uint16_t* op = p.out + ((long long)q_row * p.num_heads + head) * D + 4 * h;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t w[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const __bf16 lo = (__bf16)(o[mo][4 * g + 2 * j] * inv);
-          const __bf16 hi = (__bf16)(o[mo][4 * g + 2 * j + 1] * inv);
-          w[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-        *reinterpret_cast<uint2*>(op + 32 * mo + 8 * g) = make_uint2(w[0], w[1]);
+      for (int db = 0; db < DB; ++db) {
+        const bf16x2 lo = {(__bf16)(o[db][qb][0] * inv), (__bf16)(o[db][qb][1] * inv)};
+        const bf16x2 hi = {(__bf16)(o[db][qb][2] * inv), (__bf16)(o[db][qb][3] * inv)};
+        *reinterpret_cast<uint2*>(op + 16 * db) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
-  } else {
-    const long long row = ((long long)split * p.n_queries + q_row) * p.num_heads + head;
-    float* op = p.part_o + row * D + 4 * half;
+    } else {
+      const long long row = ((long long)split * p.n_queries + q_row) * p.num_heads + head;
+      float* op = p.part_o + row * D + 4 * h;
 #pragma unroll
-    for (int mo = 0; mo < MO; ++mo)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(op + 32 * mo + 8 * g) =
-            make_float4(o[mo][4 * g] * inv, o[mo][4 * g + 1] * inv, o[mo][4 * g + 2] * inv, o[mo][4 * g + 3] * inv);
-    if (half == 0) p.part_lse[row] = m + __log2f(ltot);
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(op + 16 * db) =
+            make_float4(o[db][qb][0] * inv, o[db][qb][1] * inv, o[db][qb][2] * inv, o[db][qb][3] * inv);
+      if (h == 0) p.part_lse[row] = m[qb] + __log2f(ltot);
+    }
   }
 }
 
@@ -288,11 +465,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     acc.w += w * v.w;
   }
   const float inv = 1.f / wsum;
-  const __bf16 b0 = (__bf16)(acc.x * inv), b1 = (__bf16)(acc.y * inv), b2 = (__bf16)(acc.z * inv),
-               b3 = (__bf16)(acc.w * inv);
-  const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-  const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-  *reinterpret_cast<uint2*>(p.out + row * D + 4 * c4) = make_uint2(w0, w1);
+  const bf16x2 lo = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv)};
+  const bf16x2 hi = {(__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
+  *reinterpret_cast<uint2*>(p.out + row * D + 4 * c4) =
+      make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 }  // namespace
