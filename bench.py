@@ -11,8 +11,16 @@ Prints one JSON line.  `value` is algorithmic attention TFLOP/s over the
 whole rollout (4 * n_q * n_k * 3072 per attention call, the convention of
 "Learning Video Generation from the Wan2.2 Source Code", Chapter 8);
 `ms_per_step` is milliseconds per rollout.  The roofline block is for the
-chunk-attention kernel on its 880-query x 19,360-key launches (chunks 19..28),
-timed with HIP events on the launch stream inside the timed rollouts.
+dominant kernel, chunk attention (the MFMA kernel plus, when the key range is
+split, its small merge kernel), over all of its launches in the timed
+rollouts, timed with HIP events on the launch stream; the 880-query x
+19,360-key launches (chunks 19..28) are also reported on their own.
+
+`--counters FETCH.csv WRITE.csv` turns two rocprofv3 --pmc runs of
+`bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration` (one for
+FETCH_SIZE, one for WRITE_SIZE) into the HBM traffic per chunk-attention
+call, scaled by what the same counters read for the plain 1 GiB copy, and
+writes it with the kernel source's hash to profiles/.
 """
 
 from __future__ import annotations
@@ -31,7 +39,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "chunk_attn_880x19360_counters.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "chunk_attn_rollout_hbm_counters.txt")
 ATTN_SOURCE = os.path.join(ROOT, "chunked_kv_attention_amd", "csrc", "chunk_attn.hip")
 
 
@@ -44,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the counters file and exit")
     return ap.parse_args()
 
 
@@ -72,9 +82,17 @@ def attn_flops(cfg, chunk):
     return 4 * cfg.tokens(chunk) * keys_of(cfg, chunk) * cfg.num_heads * cfg.head_dim
 
 
+ATTN_KERNELS = ("chunk_attn_kernel", "attn_combine_kernel")
+COPY_BYTES = 1 << 30
+
+
+def source_hash():
+    return hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+
+
 def read_counters():
-    """HBM traffic per launch from committed rocprofv3 counter runs, valid only
-    while the kernel source is unchanged."""
+    """HBM traffic per chunk-attention call from committed rocprofv3 counter
+    runs, valid only while the kernel source is unchanged."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     vals = {}
@@ -83,10 +101,63 @@ def read_counters():
         if "=" in line:
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    if vals.get("source_sha256") != src or "traffic_bytes_per_launch" not in vals:
+    if vals.get("source_sha256") != source_hash() or "traffic_bytes_per_call" not in vals:
         return None
-    return float(vals["traffic_bytes_per_launch"])
+    return float(vals["traffic_bytes_per_call"])
+
+
+def summarise_counters(fetch_csv, write_csv):
+    """Per-call HBM bytes of chunk attention from FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), each scaled by the reading of the same counter for the
+    plain 1 GiB copy (copy reads 1 GiB and writes 1 GiB)."""
+    import csv
+
+    def load(path, counter):
+        attn, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            kib = float(r["Counter_Value"])
+            if any(k in name for k in ATTN_KERNELS):
+                attn.append((int(r["Dispatch_Id"]), name, kib))
+            elif "copyBuffer" in name or "copy" in name.lower():
+                copy.append(kib)
+        return attn, copy
+
+    f_attn, f_copy = load(fetch_csv, "FETCH_SIZE")
+    w_attn, w_copy = load(write_csv, "WRITE_SIZE")
+    big_copy_f = max(f_copy)  # the 1 GiB copy dispatches
+    big_copy_w = max(w_copy)
+    fetch_scale = COPY_BYTES / (big_copy_f * 1024)
+    write_scale = COPY_BYTES / (big_copy_w * 1024)
+    calls = sum(1 for _, n, _ in f_attn if "chunk_attn_kernel" in n)
+    fetch_bytes = sum(k for _, _, k in f_attn) * 1024 * fetch_scale / calls
+    write_bytes = sum(k for _, _, k in w_attn) * 1024 * write_scale / calls
+    lines = [
+        "# HBM traffic of one chunk-attention call (chunk_attn_kernel + attn_combine_kernel),",
+        "# averaged over the 117 calls of one 1-layer 29-chunk rollout.",
+        "# Commands (run from the repository root; cd /tmp && export TMPDIR=/tmp first):",
+        "#   rocprofv3 --pmc FETCH_SIZE -d OUT_F -o fetch --output-format csv -- "
+        "python bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+        "#   rocprofv3 --pmc WRITE_SIZE -d OUT_W -o write --output-format csv -- "
+        "python bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+        "#   python bench.py --counters OUT_F/fetch_counter_collection.csv OUT_W/write_counter_collection.csv",
+        "# Scaling: the same counters read for the plain 1 GiB device copy (reads and writes 1 GiB).",
+        f"copy_fetch_kib = {big_copy_f:.0f}",
+        f"copy_write_kib = {big_copy_w:.0f}",
+        f"fetch_scale = {fetch_scale:.4f}",
+        f"write_scale = {write_scale:.4f}",
+        f"attention_calls = {calls}",
+        f"fetch_bytes_per_call = {fetch_bytes:.0f}",
+        f"write_bytes_per_call = {write_bytes:.0f}",
+        f"traffic_bytes_per_call = {fetch_bytes + write_bytes:.0f}",
+        f"source_sha256 = {source_hash()}",
+    ]
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    with open(COUNTERS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(cfg, heads):
@@ -139,6 +210,9 @@ def cpu_baseline(cfg, heads):
 
 def main():
     args = parse()
+    if args.counters:
+        summarise_counters(*args.counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the same-step chunk attention path is built and timed on a single "
               "MI355X (head-sharding across GPUs is a design note, not part of this build). Run with --gpus 1.",
@@ -223,6 +297,9 @@ def main():
     big_flops = attn_flops(cfg, 19)
     big_us = 1e3 * sum(attn_big_ms) / len(attn_big_ms)
     big_tflops = big_flops / (big_us * 1e-6) / 1e12
+    attn_us_per_call = 1e3 * attn_all_ms / (args.steps * len(calls))
+    attn_flops_per_call = total_flops / len(calls)
+    attn_tflops = attn_flops_per_call / (attn_us_per_call * 1e-6) / 1e12
     append_bytes = 6 * cfg.tokens(1) * H * d * 2
     append_us = 1e3 * sum(append_ms) / len(append_ms)
     traffic = read_counters()
@@ -266,11 +343,16 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "achieved": round(big_tflops, 2),
+            "achieved": round(attn_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(big_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
+            "kernel": "chunk attention call (chunk_attn_kernel + attn_combine_kernel when split)",
+            "launches_timed": args.steps * len(calls),
+            "flops_per_launch": attn_flops_per_call,
+            "us_per_launch": round(attn_us_per_call, 2),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         },
     }
     if not args.no_cpu_baseline:
