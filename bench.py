@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--workload", choices=["rollout1", "rollout30x2"], default="rollout1",
+                    help="rollout1: 1-layer 29-chunk rollout (default); rollout30x2: 30 layers x 2 prompts on "
+                         "2 streams")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the counters file and exit")
     return ap.parse_args()
@@ -208,6 +211,92 @@ def cpu_baseline(cfg, heads):
     }
 
 
+def rollout30x2(args):
+    """30 layers x 2 prompts on 2 streams at the 1280x704 profile: one step is
+    both prompts' full 30-layer 29-chunk rollouts (chunk -> step -> layer
+    order), 1.042 PFLOP of algorithmic attention.  Each prompt gets fresh
+    seeded q, k, v per (chunk, step), shared by its 30 layers; every layer
+    appends into and reads from its own rings, so the work is that of fully
+    distinct inputs."""
+    import torch
+
+    import chunked_kv_attention_amd as C
+
+    base = profile_config()
+    cfg = C.Config(num_layers=30, num_steps=base.num_steps, num_heads=base.num_heads, head_dim=base.head_dim,
+                   grid_h=base.grid_h, grid_w=base.grid_w, first_chunk_frames=base.first_chunk_frames,
+                   window_chunks=base.window_chunks, max_chunks=base.max_chunks)
+    H, d = cfg.num_heads, cfg.head_dim
+    calls = rollout_calls(cfg)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    inputs = [[], []]
+    for prompt in range(2):
+        for i, (_, _, chunk) in enumerate(calls):
+            gen.manual_seed(50000 * (prompt + 1) + i)
+            inputs[prompt].append([torch.randn((cfg.tokens(chunk), H, d), generator=gen, device=dev,
+                                               dtype=torch.float32).to(torch.bfloat16) for _ in range(3)])
+    caches = [C.Cache(cfg), C.Cache(cfg)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    bufs = [{n: (torch.empty((n, H, d), device=dev, dtype=torch.bfloat16),
+                 torch.empty((n, H, d), device=dev, dtype=torch.bfloat16)) for n in (cfg.tokens(0), cfg.tokens(1))}
+            for _ in range(2)]
+    torch.cuda.synchronize()
+
+    def run():
+        for c in caches:
+            c.reset()
+        for i, (kind, step, chunk) in enumerate(calls):
+            for layer in range(cfg.num_layers):
+                for prompt in range(2):
+                    q, k, v = inputs[prompt][i]
+                    qr, out = bufs[prompt][q.shape[0]]
+                    s = streams[prompt]
+                    if kind == "sink":
+                        caches[prompt].sink_build(layer, q, k, v, qr, stream=s)
+                    else:
+                        caches[prompt].rope_append(layer, step, chunk, q, k, v, qr, stream=s)
+                    caches[prompt].chunk_attention(layer, C.STEP_SINK if kind == "sink" else step, chunk, qr, out,
+                                                   stream=s)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flops = 2 * cfg.num_layers * sum(attn_flops(cfg, c) for _, _, c in calls)
+    result = {
+        "metric": "same-step chunk-attn TFLOP/s + % bf16 MFMA peak; ms per 29-chunk rollout",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "30-layer 29-chunk same-step rollout at 1280x704 for 2 prompts on 2 streams "
+                        "(24 heads x 128; inputs per prompt, chunk and step shared by the 30 layers)",
+            "global_batch": 2,
+            "seq_len": 19360,
+            "parallelism": "none (1 GPU, 2 streams)",
+            "algorithmic_tflop_per_step": round(flops / 1e12, 2),
+            "cache_gb_per_prompt": round(caches[0].arena.numel() / 1e9, 2),
+        },
+        "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "ms_per_30_layer_rollout_both_prompts": round(ms, 2),
+        "roofline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.counters:
@@ -225,6 +314,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     C.load()
+    if args.workload == "rollout30x2":
+        rollout30x2(args)
+        return
     dev = torch.device("cuda:0")
     cfg = profile_config()
     H, d = cfg.num_heads, cfg.head_dim

