@@ -10,32 +10,35 @@
 //
 // Tiling.  A workgroup is 4 waves; each wave owns 32 query rows of one head
 // (128 rows per workgroup).  Keys stream through LDS in tiles of 64: K rows
-// [64][d] and V^T [d][64], each row padded by 16 bytes.  Tiles are fetched
-// straight into LDS (global_load_lds_dwordx4, no staging registers): each
-// lane is given the global 16-byte piece that belongs at its LDS position,
-// so padding and row order cost nothing.  Two LDS buffers alternate; tile
-// t+1 is in flight while tile t is computed, with one barrier per tile.
+// [64][d] and V^T rows [d][64], unpadded, with the 16-byte chunks of every
+// row XOR-swizzled so that the MFMA operand reads (16 lanes on 16
+// consecutive rows, one logical chunk) hit 16 distinct bank groups.  Tiles
+// are fetched straight into LDS (global_load_lds_dwordx4, no staging
+// registers): each lane is given the global 16-byte piece that belongs at
+// its LDS position, so the swizzle and the permuted K-row order cost
+// nothing, and every wave issues the same number of fetches.  Two LDS
+// buffers alternate; tile t+1 is in flight while tile t is computed, with
+// one barrier per tile.
 //
 // Products use v_mfma_f32_16x16x32_bf16 (16x16 output blocks): per tile and
 // wave
 //   S^T[64 keys x 32 queries] = K_tile Q^T      8 independent 16x16 blocks
 //   O^T[d x 32 queries]      += V^T_tile P^T    2d/16 independent blocks
+//   l[32 queries]            += 1 P^T           row sums, 4 more MFMAs
 // so both products keep many accumulation chains in flight.  With the
 // queries as the N columns, a lane holds 16 scores of each of its 2 queries;
 // a query's row max needs a 4-lane exchange (lane xor 16, xor 32).  K rows
-// sit in LDS in a permuted order chosen so that (a) the 16 rows one MFMA
-// reads are consecutive LDS rows (conflict-free, immediate offsets) and (b)
-// the 8 scores a lane holds for each 32-key step of the PV product are 8
-// consecutive keys, so P goes from registers straight into the B operand and
-// V^T needs one 16-byte LDS read per lane.
+// sit in LDS in a permuted order chosen so that the 8 scores a lane holds
+// for each 32-key step of the PV product are 8 consecutive keys, so P goes
+// from registers straight into the B operand.
 //
 // Softmax.  Scores stay raw; the scale (times log2 e) is folded into one FMA
-// per score before exp2.  The running max is lazy: O and the running sum are
+// per score before exp2.  The running max is lazy: O and the running sums are
 // rescaled only when a tile raises some row's max by more than 2^8 (a
 // wave-uniform branch), otherwise the stale max is kept and P may reach 256,
-// which bf16 and the fp32 accumulators hold exactly enough.  The running sum
-// adds the bf16-rounded P with v_dot2_f32_bf16, so numerator and denominator
-// see the same weights.
+// which bf16 and the fp32 accumulators hold exactly enough.  The row sums are
+// taken on the matrix unit from the same bf16-rounded P that multiplies V, so
+// numerator and denominator see the same weights.
 //
 // Occupancy.  880 queries x 24 heads is only 168 workgroups of 128 rows for
 // 256 CUs, so the key range is split into up to 4 parts when that fills the
@@ -72,18 +75,26 @@ constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 template <int D>
 struct Tile {
-  static constexpr int kRowK = D + 8;               // bf16 per padded K row
-  static constexpr int kRowV = KT + 8;              // bf16 per padded V^T row
-  static constexpr int kChK = kRowK / 8;            // 16-byte pieces per K row (last one is padding)
-  static constexpr int kChV = kRowV / 8;
-  static constexpr int kPiecesK = KT * kChK;
-  static constexpr int kPiecesV = D * kChV;
-  static constexpr int kBlocksK = kPiecesK / 64;    // 1 KB blocks, one wave instruction each
-  static constexpr int kBlocksV = kPiecesV / 64;
-  static constexpr int kSlotsK = (kBlocksK + kWaves - 1) / kWaves;
-  static constexpr int kSlotsV = (kBlocksV + kWaves - 1) / kWaves;
-  static_assert(kPiecesK % 64 == 0 && kPiecesV % 64 == 0, "LDS tiles must be whole 1 KB blocks");
+  static constexpr int kChunksK = D / 8;              // 16-byte chunks per K row
+  static constexpr int kRowBytesK = 2 * D;
+  static constexpr int kRowBytesV = 2 * KT;           // 128: 8 chunks per V^T row
+  static constexpr int kBytesK = KT * kRowBytesK;
+  static constexpr int kBytesV = D * kRowBytesV;
+  static constexpr int kBlocksK = kBytesK / 1024;     // 1 KB blocks, one wave instruction each
+  static constexpr int kBlocksV = kBytesV / 1024;
+  static constexpr int kSlotsK = kBlocksK / kWaves;   // fetch instructions per wave per tile
+  static constexpr int kSlotsV = kBlocksV / kWaves;
+  static_assert(kBlocksK % kWaves == 0 && kBlocksV % kWaves == 0, "tiles split evenly over the waves");
 };
+
+// XOR swizzle of the 16-byte chunks of LDS row r.  Rows of 16 chunks (K at
+// d = 128) use r mod 16; rows of 8 chunks (V^T, and K at d = 64) use
+// (r / 2) mod 8: two such rows fill the 64 banks once, so rows 2m and 2m+1
+// differ in bank half and rows with different m in chunk.
+template <int Chunks>
+__device__ inline int swz(int r) {
+  return Chunks == 16 ? (r & 15) : ((r >> 1) & 7);
+}
 
 // K rows sit in LDS in a permuted order: LDS row p = 32s + 16b + 4h + i holds
 // tile key 32s + 8h + 4b + i.  MFMA block kb = 2s + b then reads LDS rows
@@ -92,18 +103,12 @@ __device__ inline int key_of_lds_row(int p) { return (p & ~31) | (((p >> 2) & 3)
 
 __device__ inline bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
-// max / sum over the 4 lanes l, l^16, l^32, l^48 that share a query
+// max over the 4 lanes l, l^16, l^32, l^48 that share a query
 __device__ inline float quad_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
-__device__ inline float quad_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // The up to three runs of this head's window, loaded once into uniform
@@ -141,39 +146,45 @@ __device__ inline Runs load_runs(const AttnParams& p, int head) {
   return R;
 }
 
-// Which LDS pieces this lane fetches: for slot i, block wave + 4i of the K
-// (or V^T) tile, piece lane of that block.
+// The piece lane l fetches for slot i of wave w: block b = w + 4i of the
+// tile, i.e. LDS byte 1024 b + 16 l = LDS row r, physical chunk pc; it holds
+// logical chunk pc ^ swz(r) of that row.
+template <int D>
+__device__ inline int k_piece_row(int w, int l, int i) {
+  return (w + kWaves * i) * (1024 / Tile<D>::kRowBytesK) + l / Tile<D>::kChunksK;
+}
+template <int D>
+__device__ inline int k_piece_chunk(int w, int l, int i) {
+  return (l % Tile<D>::kChunksK) ^ swz<Tile<D>::kChunksK>(k_piece_row<D>(w, l, i));
+}
+__device__ inline int v_piece_row(int w, int l, int i) { return (w + kWaves * i) * 8 + l / 8; }
+__device__ inline int v_piece_chunk(int w, int l, int i) { return (l % 8) ^ swz<8>(v_piece_row(w, l, i)); }
+
+// Per-lane byte offsets of this lane's pieces from a tile's first key in a
+// run; unsigned, so each fetch is a scalar base plus a 32-bit lane offset.
 template <int D>
 struct LaneSlots {
-  int k_key[Tile<D>::kSlotsK];  // tile key whose row this piece belongs to
-  int k_off[Tile<D>::kSlotsK];  // byte offset of the piece in the tile's key rows (key*D + 8*chunk)*2
-  int v_dim[Tile<D>::kSlotsV];  // head-dim row of V^T
-  int v_key[Tile<D>::kSlotsV];  // first of the piece's 8 keys in the tile
-  int v_off[Tile<D>::kSlotsV];  // byte offset in the current run: (v_dim*row_stride + v_key)*2
+  unsigned k_off[Tile<D>::kSlotsK];  // (key * d + 8 * chunk) * 2
+  unsigned v_off[Tile<D>::kSlotsV];  // (dim * row_stride + 8 * chunk) * 2 in the current run
 };
 
-template <int D>
-__device__ inline void make_slots(LaneSlots<D>& s, int wave, int lane) {
-  using T = Tile<D>;
-#pragma unroll
-  for (int i = 0; i < T::kSlotsK; ++i) {
-    const int piece = (wave + kWaves * i) * 64 + lane;
-    const int row = piece / T::kChK;
-    int ch = piece % T::kChK;
-    if (ch == T::kChK - 1) ch = 0;  // padding piece: fetch something valid, never read
-    s.k_key[i] = row < KT ? key_of_lds_row(row) : 0;
-    s.k_off[i] = (s.k_key[i] * D + 8 * ch) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < T::kSlotsV; ++i) {
-    const int piece = (wave + kWaves * i) * 64 + lane;
-    const int dim = piece / T::kChV;
-    int ch = piece % T::kChV;
-    if (ch == T::kChV - 1) ch = 0;
-    s.v_dim[i] = dim < D ? dim : 0;
-    s.v_key[i] = 8 * ch;
-    s.v_off[i] = 0;
-  }
+// Hide a per-lane value from the optimiser, so that nothing computed from it
+// is hoisted above this point (keeps the rare straddling path's address terms
+// out of the registers of the key loop).
+template <class T>
+__device__ inline void opaque(T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+}
+
+// One 16-byte-per-lane global -> LDS transfer (lane l lands at lds + 16 l).
+// The host pass of a HIP compile cannot resolve this builtin inside nested
+// device templates; only the device pass needs the body.
+__device__ inline void lds_dma16(const void* src, lds_void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#endif
 }
 
 // Sequential walk over this workgroup's keys.  The run (sink area or a run
@@ -188,25 +199,26 @@ struct RunCursor {
 };
 
 template <int D>
-__device__ inline void cursor_set(RunCursor& c, LaneSlots<D>& s, int begin, int end, const char* k, const char* vt,
-                                  int vrs) {
+__device__ inline void cursor_set(RunCursor& c, LaneSlots<D>& s, int w, int l, int begin, int end, const char* k,
+                                  const char* vt, int vrs) {
   c.begin = begin;
   c.end = end;
   c.k = k;
   c.vt = vt;
 #pragma unroll
-  for (int i = 0; i < Tile<D>::kSlotsV; ++i) s.v_off[i] = (s.v_dim[i] * vrs + s.v_key[i]) * 2;
+  for (int i = 0; i < Tile<D>::kSlotsV; ++i)
+    s.v_off[i] = (unsigned)(v_piece_row(w, l, i) * vrs + 8 * v_piece_chunk(w, l, i)) * 2u;
 }
 
 // Place the cursor on the run holding key j (uniform j).
 template <int D>
-__device__ inline void cursor_seek(const Runs& R, RunCursor& c, LaneSlots<D>& s, int j) {
+__device__ inline void cursor_seek(const Runs& R, RunCursor& c, LaneSlots<D>& s, int w, int l, int j) {
   if (j < R.e0)
-    cursor_set<D>(c, s, 0, R.e0, R.k0, R.v0, R.vrs0);
+    cursor_set<D>(c, s, w, l, 0, R.e0, R.k0, R.v0, R.vrs0);
   else if (j < R.e1)
-    cursor_set<D>(c, s, R.e0, R.e1, R.k1, R.v1, R.vrs1);
+    cursor_set<D>(c, s, w, l, R.e0, R.e1, R.k1, R.v1, R.vrs1);
   else
-    cursor_set<D>(c, s, R.e1, R.e2, R.k2, R.v2, R.vrs2);
+    cursor_set<D>(c, s, w, l, R.e1, R.e2, R.k2, R.v2, R.vrs2);
 }
 
 // Source of key j's K row / of V^T row `dim` at key j, for per-lane j.
@@ -223,40 +235,45 @@ __device__ inline const char* vt_at(const Runs& R, int dim, int j) {
 
 // Enqueue the fetch of key tile [t0, t0 + KT) into one LDS buffer pair.
 template <int D>
-__device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, int wave, int t0, int key_begin,
-                                  int key_end, uint4* sk, uint4* sv) {
+__device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, int w, int l, int t0, int key_begin,
+                                  int key_end, char* sk, char* sv) {
   using T = Tile<D>;
-  if (t0 >= c.end) cursor_seek<D>(R, c, s, t0);
+  if (t0 >= c.end) cursor_seek<D>(R, c, s, w, l, t0);
   if (t0 + KT <= c.end && t0 + KT <= key_end) {
-    const char* kb = c.k + (long long)(t0 - c.begin) * (2 * D);
-    const char* vb = c.vt + (long long)(t0 - c.begin) * 2;
+    // uniform bases made explicit (readfirstlane) so that each fetch stays
+    // scalar base + 32-bit lane offset
+    const char* kb = uni(c.k + (long long)(t0 - c.begin) * (2 * D));
+    const char* vb = uni(c.vt + (long long)(t0 - c.begin) * 2);
+    // (the offsets pass through opaque() so that their 64-bit extension is
+    // not hoisted out of the key loop, where it would double their registers)
 #pragma unroll
-    for (int i = 0; i < T::kSlotsK; ++i)
-      if (i < T::kBlocksK / kWaves || wave + kWaves * i < T::kBlocksK)
-        __builtin_amdgcn_global_load_lds(kb + s.k_off[i], (lds_void*)(sk + (wave + kWaves * i) * 64), 16, 0, 0);
+    for (int i = 0; i < T::kSlotsK; ++i) {
+      unsigned off = s.k_off[i];
+      opaque(off);
+      lds_dma16(kb + off, (lds_void*)(sk + (w + kWaves * i) * 1024));
+    }
 #pragma unroll
-    for (int i = 0; i < T::kSlotsV; ++i)
-      if (i < T::kBlocksV / kWaves || wave + kWaves * i < T::kBlocksV)
-        __builtin_amdgcn_global_load_lds(vb + s.v_off[i], (lds_void*)(sv + (wave + kWaves * i) * 64), 16, 0, 0);
+    for (int i = 0; i < T::kSlotsV; ++i) {
+      unsigned off = s.v_off[i];
+      opaque(off);
+      lds_dma16(vb + off, (lds_void*)(sv + (w + kWaves * i) * 1024));
+    }
   } else {
     // Tile straddles two runs or the end of this split's keys: per-lane
     // lookup; keys past the end fetch key_begin (finite data; masked later).
+    opaque(l);
 #pragma unroll
-    for (int i = 0; i < T::kSlotsK; ++i)
-      if (i < T::kBlocksK / kWaves || wave + kWaves * i < T::kBlocksK) {
-        int j = t0 + s.k_key[i];
-        if (j >= key_end) j = key_begin;
-        __builtin_amdgcn_global_load_lds(k_row_of<D>(R, j) + (s.k_off[i] - s.k_key[i] * 2 * D),
-                                         (lds_void*)(sk + (wave + kWaves * i) * 64), 16, 0, 0);
-      }
+    for (int i = 0; i < T::kSlotsK; ++i) {
+      int j = t0 + key_of_lds_row(k_piece_row<D>(w, l, i));
+      if (j >= key_end) j = key_begin;
+      lds_dma16(k_row_of<D>(R, j) + 16 * k_piece_chunk<D>(w, l, i), (lds_void*)(sk + (w + kWaves * i) * 1024));
+    }
 #pragma unroll
-    for (int i = 0; i < T::kSlotsV; ++i)
-      if (i < T::kBlocksV / kWaves || wave + kWaves * i < T::kBlocksV) {
-        int j = t0 + s.v_key[i];  // runs are multiples of 8 keys: a piece never straddles two runs
-        if (j >= key_end) j = key_begin;
-        __builtin_amdgcn_global_load_lds(vt_at(R, s.v_dim[i], j), (lds_void*)(sv + (wave + kWaves * i) * 64), 16,
-                                         0, 0);
-      }
+    for (int i = 0; i < T::kSlotsV; ++i) {
+      int j = t0 + 8 * v_piece_chunk(w, l, i);  // runs are multiples of 8 keys: a piece never straddles two runs
+      if (j >= key_end) j = key_begin;
+      lds_dma16(vt_at(R, v_piece_row(w, l, i), j), (lds_void*)(sv + (w + kWaves * i) * 1024));
+    }
   }
 }
 
@@ -264,11 +281,12 @@ __device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, 
 //   S^T = K_tile Q^T, online softmax per query, O^T += V^T_tile P^T.
 // S value (kb, qb)[i] is the score of tile key 32s + 8h + 4b + i (kb = 2s + b,
 // h = lane / 16) for query 16qb + lane % 16.  O value (db, qb)[i] is head dim
-// 16db + 4h + i of that query.
+// 16db + 4h + i of that query.  ka[kk] / va[ks] are this lane's operand byte
+// offsets within a K / V^T tile for 32-dim step kk / 32-key step ks.
 template <int D>
-__device__ inline void attend_tile(const char* kbase, const char* vbase, const bf16x8 (&qf)[D / 32][2],
-                                   f32x4 (&o)[D / 16][2], float (&m)[2], float (&lsum)[2], float scale_log2,
-                                   bool masked, int t0, int key_end, int h) {
+__device__ inline void attend_tile(const char* sk, const char* sv, const int (&ka)[D / 32], const int (&va)[KS],
+                                   const bf16x8 (&qf)[D / 32][2], f32x4 (&o)[D / 16][2], float (&m)[2],
+                                   float (&lsum)[2], float scale_log2, bool masked, int t0, int key_end, int h) {
   using T = Tile<D>;
   constexpr int KK = D / 32;
   constexpr int DB = D / 16;
@@ -281,14 +299,13 @@ __device__ inline void attend_tile(const char* kbase, const char* vbase, const b
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + (16 * kb * T::kRowK + 32 * kk) * 2));
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sk + kb * 16 * T::kRowBytesK + ka[kk]));
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk][qb], s[kb][qb], 0, 0, 0);
     }
 
   // Keep the K operand reads 4 groups ahead of the MFMAs that consume them
-  // (LDS latency spans several 16-cycle MFMAs); measured 3-4% faster than the
-  // compiler's default placement.
+  // (LDS latency spans several 16-cycle MFMAs).
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
   for (int j = 0; j < KB * KK - 4; ++j) {
@@ -327,7 +344,7 @@ __device__ inline void attend_tile(const char* kbase, const char* vbase, const b
     }
   }
 
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x8 pf[KS][2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -339,7 +356,7 @@ __device__ inline void attend_tile(const char* kbase, const char* vbase, const b
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], scale_log2, neg_m));
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i + 1], scale_log2, neg_m));
         const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-        lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum[qb], false);
+        lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, lsum[qb], false);
         pf[kb / 2][qb][4 * (kb % 2) + i] = pk[0];
         pf[kb / 2][qb][4 * (kb % 2) + i + 1] = pk[1];
       }
@@ -349,7 +366,7 @@ __device__ inline void attend_tile(const char* kbase, const char* vbase, const b
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(vbase + (16 * db * T::kRowV + 32 * ks) * 2));
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sv + db * 16 * T::kRowBytesV + va[ks]));
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[ks][qb], o[db][qb], 0, 0, 0);
     }
@@ -368,8 +385,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
   using T = Tile<D>;
   constexpr int KK = D / 32;
   constexpr int DB = D / 16;
-  __shared__ uint4 sk0[T::kPiecesK], sk1[T::kPiecesK];
-  __shared__ uint4 sv0[T::kPiecesV], sv1[T::kPiecesV];
+  __shared__ __attribute__((aligned(1024))) char sk0[T::kBytesK], sk1[T::kBytesK];
+  __shared__ __attribute__((aligned(1024))) char sv0[T::kBytesV], sv1[T::kBytesV];
 
   // Work unit: contiguous runs of (head, split, q-tile) per XCD.
   const int units = p.q_tiles * p.num_heads * p.n_splits;
@@ -388,14 +405,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
   // wave index as a scalar: block choices and LDS-DMA bases depend on it
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int h = lane / 16, c16 = lane % 16;
-  const int k_lane_byte = (c16 * T::kRowK + 8 * h) * 2;
-  const int v_lane_byte = (c16 * T::kRowV + 8 * h) * 2;
+  int ka[KK], va[KS];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) ka[kk] = c16 * T::kRowBytesK + 16 * ((4 * kk + h) ^ swz<T::kChunksK>(c16));
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) va[ks] = c16 * T::kRowBytesV + 16 * ((4 * ks + h) ^ swz<8>(c16));
 
   LaneSlots<D> slots;
-  make_slots<D>(slots, wave, lane);
+#pragma unroll
+  for (int i = 0; i < T::kSlotsK; ++i)
+    slots.k_off[i] =
+        (unsigned)(key_of_lds_row(k_piece_row<D>(wave, lane, i)) * D + 8 * k_piece_chunk<D>(wave, lane, i)) * 2u;
   const Runs runs = load_runs(p, head);
   RunCursor cursor;
-  cursor_seek<D>(runs, cursor, slots, key_begin);
+  cursor_seek<D>(runs, cursor, slots, wave, lane, key_begin);
 
   // Q^T B operand: lane holds head dims 32kk + 8h .. +8 of query 16qb + c16.
   bf16x8 qf[KK][2];
@@ -415,31 +438,33 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY};  // running max of scaled scores (log2 domain), per query block
-  float lsum[2] = {0.f, 0.f};           // this lane's share of the running sums
+  float lsum[2] = {0.f, 0.f};  // this lane's share of the running sums
 
-  const char* kl0 = reinterpret_cast<const char*>(sk0) + k_lane_byte;
-  const char* kl1 = reinterpret_cast<const char*>(sk1) + k_lane_byte;
-  const char* vl0 = reinterpret_cast<const char*>(sv0) + v_lane_byte;
-  const char* vl1 = reinterpret_cast<const char*>(sv1) + v_lane_byte;
-
-  fetch_tile<D>(runs, slots, cursor, wave, t_begin * KT, key_begin, key_end, sk0, sv0);
+  fetch_tile<D>(runs, slots, cursor, wave, lane, t_begin * KT, key_begin, key_end, sk0, sv0);
   for (int t = t_begin; t < t_end; t += 2) {
     // buffer 0 holds tile t; tile t+1 goes to buffer 1 while t is computed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < t_end) fetch_tile<D>(runs, slots, cursor, wave, (t + 1) * KT, key_begin, key_end, sk1, sv1);
-    attend_tile<D>(kl0, vl0, qf, o, m, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
+    if (t + 1 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 1) * KT, key_begin, key_end, sk1, sv1);
+    attend_tile<D>(sk0, sv0, ka, va, qf, o, m, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
     if (t + 1 >= t_end) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 2 < t_end) fetch_tile<D>(runs, slots, cursor, wave, (t + 2) * KT, key_begin, key_end, sk0, sv0);
-    attend_tile<D>(kl1, vl1, qf, o, m, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT, key_end, h);
+    if (t + 2 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 2) * KT, key_begin, key_end, sk0, sv0);
+    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT, key_end,
+                   h);
   }
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q_row = qt * QT + wave * 32 + 16 * qb + c16;
-    const float ltot = quad_sum(lsum[qb]);
+    float ltot = lsum[qb];
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ltot), __float_as_uint(ltot), false, false);
+      ltot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(ltot), __float_as_uint(ltot), false, false);
+      ltot = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+    }
     const float inv = 1.f / ltot;
     if (q_row >= p.n_queries) continue;
     if (p.n_splits == 1) {
