@@ -39,6 +39,13 @@ notes of the repository):
     rounded to bf16 (nearest, ties to even) where they enter attention.
     Everything after that (scores, softmax, weighted sum) is float64.
     `OracleConfig.attention_inputs = "f64"` keeps them unrounded.
+  * QK-Norm ([LG] Ch.4 "3D RoPE", detail paragraph: q and k are each passed
+    through an RMSNorm after their linear layers): the norm runs over the
+    whole projected vector of a token (all heads, H*d values -- the linear
+    layer's output), y = x / sqrt(mean(x^2) + eps) * gain with one learned
+    gain per channel; eps is an input (the pages print none; 1e-6 by
+    default).  The norm's output is a bf16 activation of the bf16 backbone,
+    so it is rounded to bf16 before the rotation.
 """
 
 from __future__ import annotations
@@ -170,6 +177,31 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 # Window membership ([MC] "Inference profile": up to W recent chunks plus the
 # first-chunk sink without duplication; same-step reads)
 # --------------------------------------------------------------------------
+
+
+# --------------------------------------------------------------------------
+# QK-Norm ([LG] Ch.4 "3D RoPE", detail paragraph)
+# --------------------------------------------------------------------------
+
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of every token's projected vector: x is [n, H, d] (or [n, H*d]);
+    the mean of squares runs over all H*d values of a token, then each channel
+    is scaled by its gain ([LG] Ch.4 "3D RoPE": q and k each go through an
+    RMSNorm after their linear layers).  float64."""
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(x.shape[0], -1)
+    g = np.asarray(gain, dtype=np.float64).reshape(-1)
+    if g.shape[0] != flat.shape[1]:
+        raise ValueError("one gain per channel of the projected vector")
+    ms = np.mean(flat * flat, axis=1, keepdims=True)
+    return (flat / np.sqrt(ms + eps) * g).reshape(x.shape)
+
+
+def qk_norm_bf16(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """The norm's bf16 output (rounded once, nearest-even), as float64 values:
+    what the rotation then reads."""
+    return round_to_bf16(rms_norm(x, gain, eps))
 
 
 def window_chunks(chunk: int, window: int) -> list:

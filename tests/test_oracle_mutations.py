@@ -98,6 +98,36 @@ def _round_ties_away(x):
 
 _ORIG_ATTEND = O.attend
 
+def _norm_per_head(x, gain, eps):
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64).reshape(x.shape[1:])
+
+
+def _norm_mean_abs(x, gain, eps):
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(x.shape[0], -1)
+    return (flat / (np.mean(np.abs(flat), axis=1, keepdims=True) + eps) * np.asarray(gain).reshape(-1)).reshape(x.shape)
+
+
+def _norm_no_gain(x, gain, eps):
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(x.shape[0], -1)
+    return (flat / np.sqrt(np.mean(flat * flat, axis=1, keepdims=True) + eps)).reshape(x.shape)
+
+
+def _norm_eps_outside_root(x, gain, eps):
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(x.shape[0], -1)
+    return (flat / (np.sqrt(np.mean(flat * flat, axis=1, keepdims=True)) + eps) * np.asarray(gain).reshape(-1)).reshape(x.shape)
+
+
+def _norm_sum_not_mean(x, gain, eps):
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(x.shape[0], -1)
+    return (flat / np.sqrt(np.sum(flat * flat, axis=1, keepdims=True) + eps) * np.asarray(gain).reshape(-1)).reshape(x.shape)
+
+
 MUTATIONS = [
     ("rope3d", _rope_sin_sign_flipped, [P.test_rope_is_complex_multiplication]),
     ("rope3d", _rope_half_split, [P.test_rope_is_complex_multiplication]),
@@ -112,6 +142,11 @@ MUTATIONS = [
     ("attention_flops", _flops_one_matmul, [P.test_flop_formula_worked_example]),
     ("round_to_bf16", _round_truncate, [P.test_round_to_bf16_ties_and_library]),
     ("round_to_bf16", _round_ties_away, [P.test_round_to_bf16_ties_and_library]),
+    ("rms_norm", _norm_per_head, [P.test_qk_norm_worked_example, P.test_qk_norm_spans_all_heads]),
+    ("rms_norm", _norm_mean_abs, [P.test_qk_norm_worked_example, P.test_qk_norm_matches_torch_rms_norm_float64]),
+    ("rms_norm", _norm_no_gain, [P.test_qk_norm_worked_example, P.test_qk_norm_unit_rms_scale_invariance_and_gain]),
+    ("rms_norm", _norm_eps_outside_root, [P.test_qk_norm_constant_vector_closed_form]),
+    ("rms_norm", _norm_sum_not_mean, [P.test_qk_norm_worked_example, P.test_qk_norm_unit_rms_scale_invariance_and_gain]),
 ]
 
 

@@ -7,6 +7,7 @@ plants plausible mistakes in the oracle and checks that these pins catch them.
 """
 
 import collections
+import os
 import itertools
 import math
 
@@ -306,3 +307,71 @@ def test_rollout_rounds_rotated_qk_only():
     cfg64 = O.OracleConfig(1, 1, 2, 64, 2, 4, 3, 2, 5, attention_inputs="f64")
     _, (_, kr64) = O.OracleRollout(cfg64).sink_pass(0, q, k, v)
     np.testing.assert_array_equal(kr64, full)
+
+
+# --------------------------------------------------------------------------
+# QK-Norm ("Learning Video Generation from the Wan2.2 Source Code", Ch.4,
+# "3D RoPE" detail paragraph): RMSNorm over each token's projected vector.
+# --------------------------------------------------------------------------
+
+
+def _read_qk_norm_golden():
+    vals = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "qk_norm_worked.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split("=", 1)
+                vals[k.strip()] = np.array([float(t) for t in v.split()])
+    return vals
+
+
+def test_qk_norm_worked_example():
+    g = _read_qk_norm_golden()
+    x = g["x"].reshape(1, 2, 2)
+    np.testing.assert_allclose(O.rms_norm(x, np.ones(4), 0.0).reshape(-1), g["unit"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.rms_norm(x, g["gain"], 0.0).reshape(-1), g["scaled"], rtol=0, atol=1e-15)
+
+
+def test_qk_norm_constant_vector_closed_form():
+    # a constant vector c*1 normalises to sign(c) / sqrt(1 + eps / c^2)
+    for c, eps in ((3.0, 0.0), (-0.5, 1e-6), (1e-3, 1e-6)):
+        x = np.full((2, 3, 8), c)
+        y = O.rms_norm(x, np.ones(24), eps)
+        np.testing.assert_allclose(y, np.sign(c) / math.sqrt(1.0 + eps / (c * c)), rtol=1e-14)
+
+
+def test_qk_norm_unit_rms_scale_invariance_and_gain():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((16, 24, 128))
+    y = O.rms_norm(x, np.ones(24 * 128), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y.reshape(16, -1) ** 2, axis=1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(O.rms_norm(7.5 * x, np.ones(3072), 0.0), y, rtol=1e-13)
+    gain = rng.standard_normal(3072)
+    np.testing.assert_allclose(O.rms_norm(x, gain, 0.0), y * gain.reshape(24, 128), rtol=1e-13)
+
+
+def test_qk_norm_spans_all_heads():
+    # one head ten times larger: the norm couples the heads (per-head norms would not)
+    x = np.ones((4, 3, 8))
+    x[:, 0] *= 10.0
+    y = O.rms_norm(x, np.ones(24), 0.0)
+    # mean of squares (8 * 100 + 16) / 24 = 34: the small heads come out at 1/sqrt(34)
+    np.testing.assert_allclose(y[:, 1:], 1.0 / math.sqrt(34.0), rtol=1e-14)
+    np.testing.assert_allclose(y[:, 0], 10.0 / math.sqrt(34.0), rtol=1e-14)
+
+
+def test_qk_norm_matches_torch_rms_norm_float64():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 24, 128))
+    gain = rng.uniform(0.5, 1.5, 3072)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x.reshape(5, -1)), (3072,), torch.from_numpy(gain), eps=1e-6)
+    np.testing.assert_allclose(O.rms_norm(x, gain, 1e-6).reshape(5, -1), ref.numpy(), rtol=1e-13)
+
+
+def test_qk_norm_bf16_output_is_rounded_norm():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3, 2, 64))
+    y = O.qk_norm_bf16(x, np.ones(128), 1e-6)
+    t = torch.from_numpy(O.rms_norm(x, np.ones(128), 1e-6)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(y, t)
