@@ -19,7 +19,8 @@ STEP_SINK = -1
 # Every symbol include/ckv.h declares.
 EXPORTS = (
     "ckv_cache_bytes", "ckv_cache_create", "ckv_cache_create_dry", "ckv_cache_reset",
-    "ckv_cache_destroy", "ckv_rope_append", "ckv_sink_build", "ckv_chunk_attention",
+    "ckv_cache_destroy", "ckv_rope_append", "ckv_sink_build", "ckv_norm_rope_append",
+    "ckv_norm_sink_build", "ckv_chunk_attention",
     "ckv_window", "ckv_ring_slot", "ckv_debug_copy_kv", "ckv_attention_splits",
     "ckv_status_string",
 )
@@ -77,6 +78,8 @@ def load() -> ctypes.CDLL:
         "ckv_cache_destroy": (I32, [P]),
         "ckv_rope_append": (I32, [P, I32, I32, I32, P, P, P, P, P]),
         "ckv_sink_build": (I32, [P, I32, P, P, P, P, P]),
+        "ckv_norm_rope_append": (I32, [P, I32, I32, I32, P, P, P, P, P, ctypes.c_float, P, P]),
+        "ckv_norm_sink_build": (I32, [P, I32, P, P, P, P, P, ctypes.c_float, P, P]),
         "ckv_chunk_attention": (I32, [P, I32, I32, I32, P, P, P]),
         "ckv_window": (I32, [P, I32, I32, I32, ctypes.POINTER(CkvSegment), I32, ctypes.POINTER(I32)]),
         "ckv_ring_slot": (I32, [P, I32, ctypes.POINTER(I32)]),
@@ -191,6 +194,32 @@ class Cache:
         _check(self._lib.ckv_sink_build(self._h, layer, self._ptr(q, sh, "q"), self._ptr(k, sh, "k"),
                                         self._ptr(v, sh, "v"), self._ptr(q_rot, sh, "q_rot"),
                                         self._stream(stream)), "ckv_sink_build")
+
+    def _gain(self, g, name):
+        if self.dry and isinstance(g, int):
+            return g
+        import torch
+        width = self.cfg.num_heads * self.cfg.head_dim
+        if not isinstance(g, torch.Tensor) or g.dtype != torch.float32 or not g.is_cuda or not g.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous float32 device tensor")
+        if g.numel() != width:
+            raise ValueError(f"{name} has {g.numel()} values, expected {width}")
+        return g.data_ptr()
+
+    def norm_rope_append(self, layer, step, chunk, q, k, v, q_gain, k_gain, eps, q_rot, stream=None):
+        sh = self._shape(chunk)
+        _check(self._lib.ckv_norm_rope_append(self._h, layer, step, chunk, self._ptr(q, sh, "q"), self._ptr(k, sh, "k"),
+                                              self._ptr(v, sh, "v"), self._gain(q_gain, "q_gain"),
+                                              self._gain(k_gain, "k_gain"), float(eps),
+                                              self._ptr(q_rot, sh, "q_rot"), self._stream(stream)),
+               "ckv_norm_rope_append")
+
+    def norm_sink_build(self, layer, q, k, v, q_gain, k_gain, eps, q_rot, stream=None):
+        sh = self._shape(0)
+        _check(self._lib.ckv_norm_sink_build(self._h, layer, self._ptr(q, sh, "q"), self._ptr(k, sh, "k"),
+                                             self._ptr(v, sh, "v"), self._gain(q_gain, "q_gain"),
+                                             self._gain(k_gain, "k_gain"), float(eps), self._ptr(q_rot, sh, "q_rot"),
+                                             self._stream(stream)), "ckv_norm_sink_build")
 
     def chunk_attention(self, layer, step, chunk, q_rot, out, stream=None):
         sh = self._shape(chunk)

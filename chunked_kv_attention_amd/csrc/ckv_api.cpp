@@ -180,9 +180,26 @@ int splits_for(int num_cus, int heads, int n_queries, int n_keys) {
   return p < 1 ? 1 : (int)p;
 }
 
+// Optional QK-Norm of an append / sink build: gains over the projected
+// vector (H * d floats each) and eps; q_gain == nullptr means no norm.
+struct QkNorm {
+  const float* q_gain = nullptr;
+  const float* k_gain = nullptr;
+  float eps = 0.f;
+};
+
+bool norm_ok(const QkNorm& n) {
+  return n.q_gain && n.k_gain && ((uintptr_t)n.q_gain % 16) == 0 && ((uintptr_t)n.k_gain % 16) == 0 &&
+         std::isfinite(n.eps) && n.eps > 0.f;
+}
+
 ckv_status rope_store(ckv_cache* c, int chunk, bf16_t* k_dst, bf16_t* vt_dst, long long k_hs, long long vt_hs,
-                      int vt_row, const void* q, const void* k, const void* v, void* q_rot, hipStream_t s) {
+                      int vt_row, const void* q, const void* k, const void* v, void* q_rot, hipStream_t s,
+                      const QkNorm& norm = QkNorm()) {
   ckv::RopeAppendParams p;
+  p.q_gain = norm.q_gain;
+  p.k_gain = norm.k_gain;
+  p.eps = norm.eps;
   p.q = (const bf16_t*)q;
   p.k = (const bf16_t*)k;
   p.v = (const bf16_t*)v;
@@ -200,6 +217,49 @@ ckv_status rope_store(ckv_cache* c, int chunk, bf16_t* k_dst, bf16_t* vt_dst, lo
   p.cos_sin = (const float*)(c->arena + c->L.tables_off);
   p.n_frames_table = c->L.frames_table;
   return ckv::launch_rope_append(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
+}
+
+ckv_status append_impl(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk, const void* q, const void* k,
+                       const void* v, void* q_rot, void* stream, const QkNorm& norm) {
+  if (!c) return CKV_E_INVALID;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(q_rot)) return CKV_E_INVALID;
+  ckv_status st = to_status(c->sched.check_append(layer, step, chunk));
+  if (st != CKV_OK) return st;
+  if (!c->dry) {
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = ensure_device(c, s)) != CKV_OK) return st;
+    const size_t d = c->cfg.head_dim;
+    if (chunk == 0) {
+      st = rope_store(c, 0, c->sink_k(layer), c->sink_vt(layer), (long long)c->L.n0 * d, (long long)d * c->L.n0,
+                      c->L.n0, q, k, v, q_rot, s, norm);
+    } else {
+      const int slot = c->sched.slot_of(chunk);
+      st = rope_store(c, chunk, c->ring_k(layer, step) + (size_t)slot * c->L.n1 * d,
+                      c->ring_vt(layer, step) + (size_t)slot * c->L.n1, (long long)c->L.ring_rows * d,
+                      (long long)d * c->L.ring_rows, c->L.ring_rows, q, k, v, q_rot, s, norm);
+    }
+    if (st != CKV_OK) return st;
+  }
+  c->sched.commit_append(layer, step, chunk);
+  return CKV_OK;
+}
+
+ckv_status sink_impl(ckv_cache* c, int32_t layer, const void* q, const void* k, const void* v, void* q_rot,
+                     void* stream, const QkNorm& norm) {
+  if (!c) return CKV_E_INVALID;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(q_rot)) return CKV_E_INVALID;
+  ckv_status st = to_status(c->sched.check_sink_build(layer));
+  if (st != CKV_OK) return st;
+  if (!c->dry) {
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = ensure_device(c, s)) != CKV_OK) return st;
+    const size_t d = c->cfg.head_dim;
+    st = rope_store(c, 0, c->sink_k(layer), c->sink_vt(layer), (long long)c->L.n0 * d, (long long)d * c->L.n0,
+                    c->L.n0, q, k, v, q_rot, s, norm);
+    if (st != CKV_OK) return st;
+  }
+  c->sched.commit_sink_build(layer);
+  return CKV_OK;
 }
 
 }  // namespace
@@ -245,46 +305,33 @@ ckv_status ckv_cache_destroy(ckv_cache* c) {
 
 ckv_status ckv_rope_append(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk, const void* q, const void* k,
                            const void* v, void* q_rot, void* stream) {
-  if (!c) return CKV_E_INVALID;
-  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(q_rot)) return CKV_E_INVALID;
-  ckv_status st = to_status(c->sched.check_append(layer, step, chunk));
-  if (st != CKV_OK) return st;
-  if (!c->dry) {
-    hipStream_t s = (hipStream_t)stream;
-    if ((st = ensure_device(c, s)) != CKV_OK) return st;
-    const size_t H = c->cfg.num_heads, d = c->cfg.head_dim;
-    if (chunk == 0) {
-      st = rope_store(c, 0, c->sink_k(layer), c->sink_vt(layer), (long long)c->L.n0 * d, (long long)d * c->L.n0,
-                      c->L.n0, q, k, v, q_rot, s);
-    } else {
-      const int slot = c->sched.slot_of(chunk);
-      st = rope_store(c, chunk, c->ring_k(layer, step) + (size_t)slot * c->L.n1 * d,
-                      c->ring_vt(layer, step) + (size_t)slot * c->L.n1, (long long)c->L.ring_rows * d,
-                      (long long)d * c->L.ring_rows, c->L.ring_rows, q, k, v, q_rot, s);
-    }
-    (void)H;
-    if (st != CKV_OK) return st;
-  }
-  c->sched.commit_append(layer, step, chunk);
-  return CKV_OK;
+  return append_impl(c, layer, step, chunk, q, k, v, q_rot, stream, QkNorm());
 }
 
 ckv_status ckv_sink_build(ckv_cache* c, int32_t layer, const void* q, const void* k, const void* v, void* q_rot,
                           void* stream) {
-  if (!c) return CKV_E_INVALID;
-  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(q_rot)) return CKV_E_INVALID;
-  ckv_status st = to_status(c->sched.check_sink_build(layer));
-  if (st != CKV_OK) return st;
-  if (!c->dry) {
-    hipStream_t s = (hipStream_t)stream;
-    if ((st = ensure_device(c, s)) != CKV_OK) return st;
-    const size_t d = c->cfg.head_dim;
-    st = rope_store(c, 0, c->sink_k(layer), c->sink_vt(layer), (long long)c->L.n0 * d, (long long)d * c->L.n0,
-                    c->L.n0, q, k, v, q_rot, s);
-    if (st != CKV_OK) return st;
-  }
-  c->sched.commit_sink_build(layer);
-  return CKV_OK;
+  return sink_impl(c, layer, q, k, v, q_rot, stream, QkNorm());
+}
+
+ckv_status ckv_norm_rope_append(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk, const void* q,
+                                const void* k, const void* v, const float* q_gain, const float* k_gain, float eps,
+                                void* q_rot, void* stream) {
+  QkNorm n;
+  n.q_gain = q_gain;
+  n.k_gain = k_gain;
+  n.eps = eps;
+  if (!norm_ok(n)) return CKV_E_INVALID;
+  return append_impl(c, layer, step, chunk, q, k, v, q_rot, stream, n);
+}
+
+ckv_status ckv_norm_sink_build(ckv_cache* c, int32_t layer, const void* q, const void* k, const void* v,
+                               const float* q_gain, const float* k_gain, float eps, void* q_rot, void* stream) {
+  QkNorm n;
+  n.q_gain = q_gain;
+  n.k_gain = k_gain;
+  n.eps = eps;
+  if (!norm_ok(n)) return CKV_E_INVALID;
+  return sink_impl(c, layer, q, k, v, q_rot, stream, n);
 }
 
 ckv_status ckv_chunk_attention(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk, const void* q_rot,

@@ -26,6 +26,13 @@ struct RopeAppendParams {
   int grid_h, grid_w;
   const float* cos_sin;      // [frames][Dt/2] | [grid_h][Dh/2] | [grid_w][Dw/2] float2 (cos, sin)
   int n_frames_table;
+  // QK-Norm (optional; null gains = q and k used as given): each token's q
+  // and k are first divided by the root of the mean of squares of their
+  // whole projected vector (H * d values) plus eps, scaled by a per-channel
+  // gain, rounded to bf16, and only then rotated.
+  const float* q_gain;       // [H * d] or null
+  const float* k_gain;       // [H * d] or null
+  float eps;
 };
 
 // Up to three runs of keys, in key order; run r holds keys [end[r-1], end[r]).

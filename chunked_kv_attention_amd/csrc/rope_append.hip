@@ -9,6 +9,14 @@
 // on the host in float64 and rounded once to float32; the rotation itself is
 // float32 with one bf16 rounding (nearest-even) at the end.
 //
+// QK-Norm ("Learning Video Generation from the Wan2.2 Source Code", Chapter 4,
+// "3D RoPE" detail paragraph: q and k each pass an RMSNorm after their linear
+// layers), when asked for: the wave that rotates a token's q and k holds all
+// of its H*d values, so it takes their mean of squares (float32, a wave
+// reduction), scales each value by 1/sqrt(mean + eps) and its channel's gain,
+// rounds to bf16 (the norm's output precision) and rotates that -- the norm
+// costs no extra pass over q and k.
+//
 // Store layout written here (read by the attention kernel):
 //   K rows  [H][rows][d]   -- one contiguous d-vector per key;
 //   V^T     [H][d][cols]   -- keys contiguous along a head-dim row, so the
@@ -63,45 +71,137 @@ __device__ inline void rotate8(const uint4& in, uint4& out, int pair0, int frame
   out = make_uint4(w_out[0], w_out[1], w_out[2], w_out[3]);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeAppendParams p) {
+// x (8 bf16) * inv * gain[0..7], rounded to bf16 once.
+__device__ inline uint4 norm8(const uint4& in, float inv, const float* __restrict__ gain) {
+  const float4 g0 = *reinterpret_cast<const float4*>(gain);
+  const float4 g1 = *reinterpret_cast<const float4*>(gain + 4);
+  const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  const uint32_t w_in[4] = {in.x, in.y, in.z, in.w};
+  uint32_t w_out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float y0 = bf16_to_f32((uint16_t)(w_in[j] & 0xFFFFu)) * inv * g[2 * j];
+    const float y1 = bf16_to_f32((uint16_t)(w_in[j] >> 16)) * inv * g[2 * j + 1];
+    w_out[j] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+  }
+  return make_uint4(w_out[0], w_out[1], w_out[2], w_out[3]);
+}
+
+// Wave sum of a float over its 64 lanes.
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ inline float sum_sq8(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = bf16_to_f32((uint16_t)(w[j] & 0xFFFFu)), b = bf16_to_f32((uint16_t)(w[j] >> 16));
+    s += a * a + b * b;
+  }
+  return s;
+}
+
+constexpr int kGroup = 8;  // 16-byte chunks a lane holds at once (512 per wave)
+
+// Two kinds of workgroup in one launch.
+//  * The first qk_blocks: one wave per token, covering q and k of all heads
+//    (the token's whole projected vector, H*d values): consecutive lanes take
+//    consecutive 16-byte chunks, so loads and stores are fully coalesced, and
+//    with the QK-Norm the wave holds every value of the token for its mean of
+//    squares (a wave reduction) before it scales, rounds and rotates.
+//  * The rest: V^T for 64 tokens of one head, transposed through LDS.
+template <int D, bool kNorm>
+__global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeAppendParams p, int qk_blocks) {
   constexpr int C8 = D / 8;                   // 16-byte chunks per head row
   constexpr int Pt = (D - 4 * (D / 6)) / 2;
   constexpr int Ph = (2 * (D / 6)) / 2;
   __shared__ uint16_t sv[kTok][D + 8];        // V tile, padded rows
-
-  const int head = blockIdx.y;
-  const int tok0 = blockIdx.x * kTok;
   const int H = p.num_heads;
-  const int per_frame = p.grid_h * p.grid_w;
   const float2* tab_t = reinterpret_cast<const float2*>(p.cos_sin);
   const float2* tab_h = tab_t + p.n_frames_table * Pt;
   const float2* tab_w = tab_h + p.grid_h * Ph;
 
-  // q and k: rotate 8 elements (4 pairs) per 16-byte chunk; v: stage in LDS.
+  if ((int)blockIdx.x < qk_blocks) {
+    const int tok = blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
+    if (tok >= p.n_tokens) return;  // no barrier on this path
+    const int per_frame = p.grid_h * p.grid_w;
+    const int fl = tok / per_frame;
+    const int rem = tok - fl * per_frame;
+    const int row = rem / p.grid_w;
+    const int col = rem - row * p.grid_w;
+    const int frame = p.first_frame + fl;
+    const int W8 = H * C8;                    // chunks per token
+    const long long base = (long long)tok * H * D;
+    float inv_q = 1.f, inv_k = 1.f;
+    if (kNorm && W8 > 64 * kGroup) {          // wide tokens: a first pass for the norm
+      float sq = 0.f, sk = 0.f;
+      for (int c = lane; c < W8; c += 64) {
+        sq += sum_sq8(*reinterpret_cast<const uint4*>(p.q + base + c * 8));
+        sk += sum_sq8(*reinterpret_cast<const uint4*>(p.k + base + c * 8));
+      }
+      inv_q = 1.f / sqrtf(wave_sum(sq) / (H * D) + p.eps);
+      inv_k = 1.f / sqrtf(wave_sum(sk) / (H * D) + p.eps);
+    }
+    for (int g0 = 0; g0 < W8; g0 += 64 * kGroup) {
+      uint4 qv[kGroup], kv[kGroup];
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const int c = g0 + lane + 64 * i;
+        if (c < W8) {
+          qv[i] = *reinterpret_cast<const uint4*>(p.q + base + c * 8);
+          kv[i] = *reinterpret_cast<const uint4*>(p.k + base + c * 8);
+        }
+      }
+      if (kNorm && W8 <= 64 * kGroup) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i)
+          if (g0 + lane + 64 * i < W8) {
+            sq += sum_sq8(qv[i]);
+            sk += sum_sq8(kv[i]);
+          }
+        inv_q = 1.f / sqrtf(wave_sum(sq) / (H * D) + p.eps);
+        inv_k = 1.f / sqrtf(wave_sum(sk) / (H * D) + p.eps);
+      }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const int c = g0 + lane + 64 * i;
+        if (c < W8) {
+          const int head = c / C8, cc = c % C8;
+          uint4 qn = qv[i], kn = kv[i];
+          if (kNorm) {
+            qn = norm8(qn, inv_q, p.q_gain + c * 8);  // channel c*8.. = head*d + 8*cc..
+            kn = norm8(kn, inv_k, p.k_gain + c * 8);
+          }
+          uint4 qo, ko;
+          rotate8<D>(qn, qo, cc * 4, frame, row, col, tab_t, tab_h, tab_w);
+          rotate8<D>(kn, ko, cc * 4, frame, row, col, tab_t, tab_h, tab_w);
+          *reinterpret_cast<uint4*>(p.q_rot + base + c * 8) = qo;
+          *reinterpret_cast<uint4*>(p.k_dst + head * p.k_head_stride + (long long)tok * D + cc * 8) = ko;
+        }
+      }
+    }
+    return;
+  }
+
+  const int vb = blockIdx.x - qk_blocks;
+  const int tok_blocks = (p.n_tokens + kTok - 1) / kTok;
+  const int head = vb / tok_blocks;
+  const int tok0 = (vb % tok_blocks) * kTok;
 #pragma unroll
   for (int it = 0; it < (kTok * C8) / kThreads; ++it) {
     const int idx = threadIdx.x + it * kThreads;
     const int t = idx / C8;
     const int c = idx % C8;
     const int tok = tok0 + t;
-    if (tok < p.n_tokens) {
-      const int fl = tok / per_frame;
-      const int rem = tok - fl * per_frame;
-      const int row = rem / p.grid_w;
-      const int col = rem - row * p.grid_w;
-      const int frame = p.first_frame + fl;
-      const long long src = ((long long)tok * H + head) * D + c * 8;
-      const uint4 qv = *reinterpret_cast<const uint4*>(p.q + src);
-      const uint4 kv = *reinterpret_cast<const uint4*>(p.k + src);
-      const uint4 vv = *reinterpret_cast<const uint4*>(p.v + src);
-      uint4 qo, ko;
-      rotate8<D>(qv, qo, c * 4, frame, row, col, tab_t, tab_h, tab_w);
-      rotate8<D>(kv, ko, c * 4, frame, row, col, tab_t, tab_h, tab_w);
-      *reinterpret_cast<uint4*>(p.q_rot + src) = qo;
-      *reinterpret_cast<uint4*>(p.k_dst + head * p.k_head_stride + (long long)tok * D + c * 8) = ko;
-      *reinterpret_cast<uint4*>(&sv[t][c * 8]) = vv;
-    }
+    if (tok < p.n_tokens)
+      *reinterpret_cast<uint4*>(&sv[t][c * 8]) =
+          *reinterpret_cast<const uint4*>(p.v + ((long long)tok * H + head) * D + c * 8);
   }
   __syncthreads();
   // V^T: each thread writes 8 consecutive tokens of one head-dim row.
@@ -137,11 +237,19 @@ __global__ __launch_bounds__(256) void copy_kv_kernel(CopyKVParams p) {
 }  // namespace
 
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s) {
-  dim3 grid((p.n_tokens + kTok - 1) / kTok, p.num_heads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(rope_append_kernel<128>, grid, dim3(kThreads), 0, s, p);
+  if (p.n_tokens <= 0 || p.num_heads <= 0) return hipErrorInvalidValue;
+  const int qk_blocks = (p.n_tokens + kThreads / 64 - 1) / (kThreads / 64);
+  const int v_blocks = ((p.n_tokens + kTok - 1) / kTok) * p.num_heads;
+  const dim3 grid(qk_blocks + v_blocks);
+  const bool norm = p.q_gain != nullptr;
+  if (head_dim == 128 && norm)
+    hipLaunchKernelGGL((rope_append_kernel<128, true>), grid, dim3(kThreads), 0, s, p, qk_blocks);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((rope_append_kernel<128, false>), grid, dim3(kThreads), 0, s, p, qk_blocks);
+  else if (head_dim == 64 && norm)
+    hipLaunchKernelGGL((rope_append_kernel<64, true>), grid, dim3(kThreads), 0, s, p, qk_blocks);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(rope_append_kernel<64>, grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((rope_append_kernel<64, false>), grid, dim3(kThreads), 0, s, p, qk_blocks);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -138,6 +138,27 @@ ckv_status ckv_rope_append(ckv_cache* c, int32_t layer, int32_t step, int32_t ch
 ckv_status ckv_sink_build(ckv_cache* c, int32_t layer, const void* q, const void* k,
                           const void* v, void* q_rot, void* stream);
 
+/* The same two calls with the QK-Norm in front ("Learning Video Generation
+ * from the Wan2.2 Source Code", Chapter 4, "3D RoPE" detail paragraph: q and k
+ * each pass an RMSNorm after their linear layers).  q and k are the raw
+ * projections [n_tokens][H][d] bf16; each token's whole projected vector (all
+ * H*d values) is divided by sqrt(mean of its squares + eps) and multiplied
+ * channel-wise by q_gain / k_gain, rounded to bf16 (the norm's output
+ * precision), and then rotated and stored exactly as ckv_rope_append /
+ * ckv_sink_build do.  v is not normalised.
+ *   q_gain, k_gain: device float32 [H*d] (channel h*d + i is head h, dim i),
+ *                   16-byte aligned, read during the call (keep them alive
+ *                   until the stream passes it).
+ *   eps: finite and > 0 (else CKV_E_INVALID, nothing launched).
+ * Order and state rules and all other errors are those of the plain calls. */
+ckv_status ckv_norm_rope_append(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk,
+                                const void* q, const void* k, const void* v,
+                                const float* q_gain, const float* k_gain, float eps,
+                                void* q_rot, void* stream);
+ckv_status ckv_norm_sink_build(ckv_cache* c, int32_t layer, const void* q, const void* k,
+                               const void* v, const float* q_gain, const float* k_gain, float eps,
+                               void* q_rot, void* stream);
+
 /* Chunk attention: out = softmax(scale * q_rot K_win^T) V_win per head, no
  * mask, with K_win/V_win gathered in place from
  *   chunk == 0, step in [0,S): the chunk's own step-`step` K/V (needs that

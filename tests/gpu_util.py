@@ -79,8 +79,13 @@ class Rollout:
     same seeded bf16 inputs, and compares each attention output (all rows, or
     a sample of rows when `rows_per_call` is set)."""
 
-    def __init__(self, cfg: C.Config, base_seed=0, prompt=0, rows_per_call=None, stream=None, also_f64=False):
+    def __init__(self, cfg: C.Config, base_seed=0, prompt=0, rows_per_call=None, stream=None, also_f64=False,
+                 qk_norm=None):
         self.cfg = cfg
+        # optional QK-Norm in front of the rotation: (q_gain, k_gain, eps), gains float32 [H*d]
+        self.qk_norm = qk_norm
+        if qk_norm is not None:
+            self.gains_dev = tuple(torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).cuda() for g in qk_norm[:2])
         self.cache = C.Cache(cfg)
         self.ocfg = O.OracleConfig(cfg.num_layers, cfg.num_steps, cfg.num_heads, cfg.head_dim, cfg.grid_h,
                                    cfg.grid_w, cfg.first_chunk_frames, cfg.window_chunks, cfg.max_chunks,
@@ -117,10 +122,16 @@ class Rollout:
         out = torch.empty_like(q)
         s = self.stream
         if kind == "sink":
-            self.cache.sink_build(layer, q, k, v, qr, stream=s)
+            if self.qk_norm is None:
+                self.cache.sink_build(layer, q, k, v, qr, stream=s)
+            else:
+                self.cache.norm_sink_build(layer, q, k, v, *self.gains_dev, self.qk_norm[2], qr, stream=s)
             self.cache.chunk_attention(layer, C.STEP_SINK, 0, qr, out, stream=s)
         else:
-            self.cache.rope_append(layer, step, chunk, q, k, v, qr, stream=s)
+            if self.qk_norm is None:
+                self.cache.rope_append(layer, step, chunk, q, k, v, qr, stream=s)
+            else:
+                self.cache.norm_rope_append(layer, step, chunk, q, k, v, *self.gains_dev, self.qk_norm[2], qr, stream=s)
             self.cache.chunk_attention(layer, step, chunk, qr, out, stream=s)
         return qr, out
 
@@ -132,6 +143,9 @@ class Rollout:
         if self.stream is not None:
             self.stream.synchronize()  # inputs were allocated on the current stream
         q, k, v = (I.bf16_bits_to_f64(b) for b in bits)
+        if self.qk_norm is not None:
+            gq, gk, eps = self.qk_norm
+            q, k = O.qk_norm_bf16(q, gq, eps), O.qk_norm_bf16(k, gk, eps)
         # unchecked calls only record K/V in the oracle: attend one row
         rows = self._rows(q.shape[0], (layer, step, chunk, kind)) if check else np.array([0])
         refs = []

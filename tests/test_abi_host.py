@@ -198,3 +198,24 @@ def test_attention_splits_policy():
     assert cache.attention_splits(2640, 2640) == 1
     # never fewer than 4 key tiles per split
     assert cache.attention_splits(880, 64 * 7) == 1
+
+
+def test_norm_entry_points_validate_and_follow_the_schedule():
+    cache = C.Cache(TINY, dry=True)
+    a = (FAKE, FAKE, FAKE)
+    g = (FAKE, FAKE)
+    # arguments of the norm: eps finite and > 0, gains non-null and 16-byte aligned
+    for eps in (0.0, -1e-6, float("nan"), float("inf")):
+        _expect(C.CKV_E_INVALID, cache.norm_sink_build, 0, *a, *g, eps, FAKE)
+    _expect(C.CKV_E_INVALID, cache.norm_sink_build, 0, *a, 0, FAKE, 1e-6, FAKE)
+    _expect(C.CKV_E_INVALID, cache.norm_sink_build, 0, *a, FAKE, FAKE + 4, 1e-6, FAKE)
+    # the norm variants obey the plain calls' schedule rules
+    _expect(C.CKV_E_STATE, cache.norm_rope_append, 0, 0, 1, *a, *g, 1e-6, FAKE)  # before the sink
+    cache.norm_rope_append(0, 0, 0, *a, *g, 1e-6, FAKE)
+    cache.chunk_attention(0, 0, 0, FAKE, FAKE)
+    cache.norm_sink_build(0, *a, *g, 1e-6, FAKE)
+    _expect(C.CKV_E_STATE, cache.norm_sink_build, 0, *a, *g, 1e-6, FAKE)  # once per rollout
+    _expect(C.CKV_E_ORDER, cache.norm_rope_append, 0, 0, 2, *a, *g, 1e-6, FAKE)
+    cache.norm_rope_append(0, 0, 1, *a, *g, 1e-6, FAKE)
+    cache.rope_append(0, 0, 2, *a, FAKE)  # plain and norm appends share one ring order
+    cache.chunk_attention(0, 0, 2, FAKE, FAKE)

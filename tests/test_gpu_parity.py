@@ -75,6 +75,82 @@ def test_rope_append_tiny():
     _rope_case(TINY, [0, 1, 2, 3])
 
 
+# ------------------------------------------------ QK-Norm + RoPE + append --
+
+def _gains(cfg, seed):
+    """Seeded per-channel gains (float32), q and k."""
+    rng = np.random.default_rng(seed)
+    w = cfg.num_heads * cfg.head_dim
+    return [rng.normal(1.0, 0.3, w).astype(np.float32) for _ in range(2)]
+
+
+def _norm_rope_errors(got_bits, x_bits, gain, eps, pos, theta):
+    """QK-Norm then RoPE against the oracle.  y = bf16(rms_norm(x)) is what the
+    oracle rotates; the kernel forms y in float32 and may land one bf16 ulp
+    away where the exact value sits within float32 error of a rounding
+    boundary, so at most 0.1% of elements may exceed the RoPE bound of
+    _rope_errors, and only by the rotation of such a 1-ulp change of the pair.
+    Returns the fraction equal to the oracle's rounded value."""
+    y = O.qk_norm_bf16(I.bf16_bits_to_f64(x_bits), gain, eps)
+    ref = O.rope3d(y, pos, theta)
+    got = I.bf16_bits_to_f64(got_bits)
+    ulp = lambda a: np.ldexp(1.0, (np.frexp(np.maximum(np.abs(a), 2.0 ** -120))[1] - 1) - 7)  # noqa: E731
+    pair = np.repeat(np.abs(y[..., 0::2]) + np.abs(y[..., 1::2]), 2, axis=-1)
+    pair_ulp = np.repeat(ulp(y[..., 0::2]) + ulp(y[..., 1::2]), 2, axis=-1)
+    tight = 0.5 * ulp(ref) + 2.0 ** -21 * pair
+    err = np.abs(got - ref)
+    assert (err > tight).mean() <= 1e-3, (err > tight).mean()
+    loose = tight + pair_ulp
+    over = err > loose
+    assert not over.any(), (np.argwhere(over)[:5], got[over][:5], ref[over][:5])
+    return float((got == O.round_to_bf16(ref)).mean())
+
+
+def _norm_rope_case(cfg: C.Config, chunks, eps=1e-6):
+    cache = C.Cache(cfg)
+    H, d = cfg.num_heads, cfg.head_dim
+    gq, gk = _gains(cfg, 11)
+    gq_dev, gk_dev = (torch.from_numpy(g).cuda() for g in (gq, gk))
+    for c in chunks:
+        n = cfg.tokens(c)
+        key = dict(base_seed=9, layer=0, chunk=c, step_code=0 if c else cfg.num_steps)
+        qb, kb, vb = I.draw_qkv_bits(n, H, d, **key)
+        q, k, v = (G.to_dev(b) for b in (qb, kb, vb))
+        qr = torch.empty_like(q)
+        if c == 0:
+            cache.norm_sink_build(0, q, k, v, gq_dev, gk_dev, eps, qr)
+        else:
+            cache.norm_rope_append(0, 0, c, q, k, v, gq_dev, gk_dev, eps, qr)
+        k_out, v_out = torch.empty_like(q), torch.empty_like(q)
+        cache.debug_copy_kv(0, C.STEP_SINK if c == 0 else 0, c, k_out, v_out)
+        torch.cuda.synchronize()
+        pos = O.token_positions(c, cfg.grid_h, cfg.grid_w, cfg.first_chunk_frames)
+        exact_q = _norm_rope_errors(G.bits_of(qr), qb, gq, eps, pos, cfg.rope_theta)
+        exact_k = _norm_rope_errors(G.bits_of(k_out), kb, gk, eps, pos, cfg.rope_theta)
+        assert exact_q > 0.98 and exact_k > 0.98, (c, exact_q, exact_k)
+        np.testing.assert_array_equal(G.bits_of(v_out), vb)  # V is not normalised
+        print(f"  norm+rope chunk {c}: {exact_q:.4f} / {exact_k:.4f} of q / k equal to the rounded oracle", flush=True)
+
+
+def test_norm_rope_append_tiny():
+    _norm_rope_case(TINY, [0, 1, 2, 3])
+
+
+def test_norm_rope_append_profile_shape():
+    # 24 heads x 128: the norm spans 3072 values per token
+    _norm_rope_case(PROFILE1, [0, 1, 2], eps=1e-6)
+
+
+def test_norm_tiny_rollout_every_chunk_and_step():
+    """The tiny rollout with QK-Norm in front of every append and the sink:
+    every output element of every call against the oracle."""
+    gq, gk = _gains(TINY, 12)
+    r = G.Rollout(TINY, qk_norm=(gq, gk, 1e-6))
+    r.run_first_chunk()
+    r.run_chunks(range(1, 6))
+    print(f"tiny norm rollout worst: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
+
+
 def test_rope_append_profile_shape():
     # full 22 x 40 grid, 24 heads: the sink (frames 0..2) and chunks 1, 2
     _rope_case(PROFILE1, [0, 1, 2])
