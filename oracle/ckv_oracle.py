@@ -11,8 +11,10 @@ Sources (web pages; cited by title and section):
         and the paragraph after it (same-step KV, sink, schedule).
   [LG]  "Learning Video Generation from the Wan2.2 Source Code": Chapter 2
         (VAE strides, latent-shape formula, the 4n+1 rule, the 5B VAE),
-        Chapter 4 ("From Latent to Token", "3D RoPE: Letting Tokens Know Where
-        They Are"), Chapter 8 ("What Does 75600^2 Actually Mean?").
+        Chapter 3 ("Where Did the Prompt Go?": the text context), Chapter 4
+        ("From Latent to Token", "3D RoPE: Letting Tokens Know Where They
+        Are", the block forward pass), Chapter 8 ("What Does 75600^2
+        Actually Mean?").
   [TI]  Wan2.2 docs index, "Wan2.2-TI2V-5B High-Compression Video Generation"
         (4x16x16 VAE, 4x32x32 with patchify) and "Run TI2V generation"
         (720P is 1280*704).
@@ -247,6 +249,19 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndar
         p /= p.sum(axis=1, keepdims=True)
         out[:, h, :] = p @ vh[h]
     return out
+
+
+def cross_attention(q: np.ndarray, k_text: np.ndarray, v_text: np.ndarray, n_text: int, scale: float) -> np.ndarray:
+    """Cross-attention of video tokens to the text context ([LG] Ch.3 "Where
+    Did the Prompt Go?": the prompt becomes up to 512 context vectors, trimmed
+    to its real length, and every layer's cross-attention takes the video
+    tokens as queries and the context as keys/values; Ch.4's block code passes
+    the context lengths to it).  No position rotation, no mask beyond the
+    real length: plain attention over the first n_text context rows.
+    q [nq, H, d]; k_text, v_text [>= n_text, H, d]."""
+    if not 1 <= n_text <= np.asarray(k_text).shape[0]:
+        raise ValueError("n_text must be within the context")
+    return attend(q, np.asarray(k_text)[:n_text], np.asarray(v_text)[:n_text], scale)
 
 
 # --------------------------------------------------------------------------

@@ -128,6 +128,10 @@ def _norm_sum_not_mean(x, gain, eps):
     return (flat / np.sqrt(np.sum(flat * flat, axis=1, keepdims=True) + eps) * np.asarray(gain).reshape(-1)).reshape(x.shape)
 
 
+def _cross_over_padding(q, k_text, v_text, n_text, scale):
+    return O.attend(q, k_text, v_text, scale)
+
+
 MUTATIONS = [
     ("rope3d", _rope_sin_sign_flipped, [P.test_rope_is_complex_multiplication]),
     ("rope3d", _rope_half_split, [P.test_rope_is_complex_multiplication]),
@@ -146,6 +150,7 @@ MUTATIONS = [
     ("rms_norm", _norm_mean_abs, [P.test_qk_norm_worked_example, P.test_qk_norm_matches_torch_rms_norm_float64]),
     ("rms_norm", _norm_no_gain, [P.test_qk_norm_worked_example, P.test_qk_norm_unit_rms_scale_invariance_and_gain]),
     ("rms_norm", _norm_eps_outside_root, [P.test_qk_norm_constant_vector_closed_form]),
+    ("cross_attention", _cross_over_padding, [P.test_cross_attention_uses_only_the_real_context_length]),
     ("rms_norm", _norm_sum_not_mean, [P.test_qk_norm_worked_example, P.test_qk_norm_unit_rms_scale_invariance_and_gain]),
 ]
 

@@ -375,3 +375,38 @@ def test_qk_norm_bf16_output_is_rounded_norm():
     y = O.qk_norm_bf16(x, np.ones(128), 1e-6)
     t = torch.from_numpy(O.rms_norm(x, np.ones(128), 1e-6)).to(torch.bfloat16).to(torch.float64).numpy()
     np.testing.assert_array_equal(y, t)
+
+
+# --------------------------------------------------------------------------
+# Cross-attention to the text context ("Learning Video Generation from the
+# Wan2.2 Source Code", Ch.3 "Where Did the Prompt Go?")
+# --------------------------------------------------------------------------
+
+
+def test_cross_attention_uses_only_the_real_context_length():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((5, 2, 16))
+    k = rng.standard_normal((12, 2, 16))
+    v = rng.standard_normal((12, 2, 16))
+    out = O.cross_attention(q, k, v, 7, 0.25)
+    # rows past the real length (padding) change nothing
+    k2, v2 = k.copy(), v.copy()
+    k2[7:] = 100.0
+    v2[7:] = -100.0
+    np.testing.assert_array_equal(O.cross_attention(q, k2, v2, 7, 0.25), out)
+    # brute force over the 7 real keys
+    ref = np.empty_like(out)
+    for i in range(5):
+        for h in range(2):
+            z = [0.25 * sum(q[i, h, e] * k[j, h, e] for e in range(16)) for j in range(7)]
+            w = [math.exp(t - max(z)) for t in z]
+            ref[i, h] = sum(w[j] * v[j, h] for j in range(7)) / sum(w)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_cross_attention_single_context_token():
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((3, 4, 8))
+    k = rng.standard_normal((1, 4, 8))
+    v = rng.standard_normal((1, 4, 8))
+    np.testing.assert_allclose(O.cross_attention(q, k, v, 1, 0.5), np.broadcast_to(v, (3, 4, 8)), rtol=0, atol=1e-15)
