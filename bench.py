@@ -26,6 +26,7 @@ writes it with the kernel source's hash to profiles/.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -348,6 +349,33 @@ def norm_append_and_copy(C, cfg, dev, stream, inputs, calls):
              "note": "device-to-device copy moving the append's byte count (half read, half written), event-timed"})
 
 
+def cross_attention_timing(C, cfg, dev, stream):
+    """Cross-attention of an 880-token chunk to a 512-row text context
+    (seeded N(0,1) bf16), 50 calls after warm-up, event-timed."""
+    import torch
+    H, d = cfg.num_heads, cfg.head_dim
+    g = torch.Generator(device=dev)
+    g.manual_seed(88)
+    k, v = (torch.randn((512, H, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    q = torch.randn((880, H, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    cache = C.Cache(dataclasses.replace(cfg, num_layers=1, num_steps=1))
+    cache.text_store(0, k, v, stream=stream)
+    for _ in range(5):
+        cache.cross_attention(0, 1, q, out, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(50):
+        cache.cross_attention(0, 1, q, out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 50
+    flops = 4 * 880 * 512 * H * d
+    return {"us_per_call": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+            "pct_bf16_peak": round(100 * flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "key_splits": cache.attention_splits(880, 512)}
+
+
 def main():
     args = parse()
     if args.counters:
@@ -500,6 +528,7 @@ def main():
     }
     result["norm_rope_append_880"], result["device_copy_same_bytes"] = norm_append_and_copy(
         C, cfg, dev, stream, inputs, calls)
+    result["cross_attn_880x512"] = cross_attention_timing(C, cfg, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
     print(json.dumps(result), flush=True)

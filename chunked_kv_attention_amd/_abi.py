@@ -15,12 +15,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libckv.so")
 
 CKV_OK, CKV_E_INVALID, CKV_E_ORDER, CKV_E_STATE, CKV_E_ARENA, CKV_E_HIP = range(6)
 STEP_SINK = -1
+MAX_TEXT_TOKENS = 512
 
 # Every symbol include/ckv.h declares.
 EXPORTS = (
     "ckv_cache_bytes", "ckv_cache_create", "ckv_cache_create_dry", "ckv_cache_reset",
     "ckv_cache_destroy", "ckv_rope_append", "ckv_sink_build", "ckv_norm_rope_append",
-    "ckv_norm_sink_build", "ckv_chunk_attention",
+    "ckv_norm_sink_build", "ckv_chunk_attention", "ckv_text_store", "ckv_cross_attention",
     "ckv_window", "ckv_ring_slot", "ckv_debug_copy_kv", "ckv_attention_splits",
     "ckv_status_string",
 )
@@ -81,6 +82,8 @@ def load() -> ctypes.CDLL:
         "ckv_norm_rope_append": (I32, [P, I32, I32, I32, P, P, P, P, P, ctypes.c_float, P, P]),
         "ckv_norm_sink_build": (I32, [P, I32, P, P, P, P, P, ctypes.c_float, P, P]),
         "ckv_chunk_attention": (I32, [P, I32, I32, I32, P, P, P]),
+        "ckv_text_store": (I32, [P, I32, P, P, I32, P]),
+        "ckv_cross_attention": (I32, [P, I32, I32, P, P, P]),
         "ckv_window": (I32, [P, I32, I32, I32, ctypes.POINTER(CkvSegment), I32, ctypes.POINTER(I32)]),
         "ckv_ring_slot": (I32, [P, I32, ctypes.POINTER(I32)]),
         "ckv_debug_copy_kv": (I32, [P, I32, I32, I32, P, P, P]),
@@ -226,6 +229,22 @@ class Cache:
         _check(self._lib.ckv_chunk_attention(self._h, layer, step, chunk, self._ptr(q_rot, sh, "q_rot"),
                                              self._ptr(out, sh, "out"), self._stream(stream)),
                "ckv_chunk_attention")
+
+    def text_store(self, layer, k_text, v_text, stream=None):
+        """Store the layer's context: k_text, v_text [n_text][H][d] bf16 device tensors."""
+        n = int(k_text.shape[0])
+        sh = (n, self.cfg.num_heads, self.cfg.head_dim)
+        _check(self._lib.ckv_text_store(self._h, layer, self._ptr(k_text, sh, "k_text"), self._ptr(v_text, sh, "v_text"),
+                                        n, self._stream(stream)), "ckv_text_store")
+
+    def text_store_rows(self, layer, k_ptr, v_ptr, n_text, stream=None):
+        """Raw-pointer form (dry caches and tests of the argument checks)."""
+        _check(self._lib.ckv_text_store(self._h, layer, k_ptr, v_ptr, n_text, self._stream(stream)), "ckv_text_store")
+
+    def cross_attention(self, layer, chunk, q, out, stream=None):
+        sh = self._shape(chunk)
+        _check(self._lib.ckv_cross_attention(self._h, layer, chunk, self._ptr(q, sh, "q"), self._ptr(out, sh, "out"),
+                                             self._stream(stream)), "ckv_cross_attention")
 
     def window(self, layer, step, chunk):
         segs = (CkvSegment * 4)()

@@ -37,6 +37,7 @@ struct Layout {
   size_t sink_off = 0, sink_layer_bytes = 0;
   size_t ring_off = 0, ring_bytes = 0;  // per (layer, step)
   size_t part_o_off = 0, part_lse_off = 0, scratch_queries = 0;
+  size_t text_off = 0, text_layer_bytes = 0;  // per layer: context K [H][max][d], V^T [H][d][max]
   size_t total = 0;
 };
 
@@ -83,6 +84,9 @@ Layout layout_of(const ckv_config* c) {
   off = align_up(off + sizeof(float) * kMaxSplits * L.scratch_queries * H * d);
   L.part_lse_off = off;
   off = align_up(off + sizeof(float) * kMaxSplits * L.scratch_queries * H);
+  L.text_off = off;
+  L.text_layer_bytes = align_up(2 * H * (size_t)CKV_MAX_TEXT_TOKENS * d * sizeof(bf16_t));
+  off += L.text_layer_bytes * c->num_layers;
   L.total = off;
   return L;
 }
@@ -99,12 +103,13 @@ struct ckv_cache {
   std::vector<float> tables;  // float2 (cos, sin), rounded once from float64
   bool tables_uploaded;
   int num_cus;
+  std::vector<int> text_len;  // per layer: context rows stored (0 = none)
 
   ckv_cache(const ckv_config& c, bool is_dry, char* a, size_t bytes)
       : cfg(c), dry(is_dry), arena(a), arena_bytes(bytes), L(layout_of(&c)),
         sched(c.num_layers, c.num_steps, c.window_chunks, c.max_chunks, c.first_chunk_frames * c.grid_h * c.grid_w,
               c.grid_h * c.grid_w),
-        tables_uploaded(false), num_cus(0) {}
+        tables_uploaded(false), num_cus(0), text_len(c.num_layers, 0) {}
 
   // 3D RoPE angle tables ("Learning Video Generation from the Wan2.2 Source
   // Code", Chapter 4, "3D RoPE"): per band of width D, pair j rotates by
@@ -135,6 +140,8 @@ struct ckv_cache {
   bf16_t* ring_vt(int layer, int step) const {
     return ring_k(layer, step) + (size_t)cfg.num_heads * L.ring_rows * cfg.head_dim;
   }
+  bf16_t* text_k(int layer) const { return (bf16_t*)(arena + L.text_off + L.text_layer_bytes * layer); }
+  bf16_t* text_vt(int layer) const { return text_k(layer) + (size_t)cfg.num_heads * CKV_MAX_TEXT_TOKENS * cfg.head_dim; }
   float scale() const { return cfg.softmax_scale > 0 ? cfg.softmax_scale : 1.0f / std::sqrt((float)cfg.head_dim); }
   int tokens(int chunk) const { return chunk == 0 ? L.n0 : L.n1; }
 };
@@ -294,6 +301,7 @@ ckv_status ckv_cache_create_dry(const ckv_config* cfg, ckv_cache** out) {
 ckv_status ckv_cache_reset(ckv_cache* c) {
   if (!c) return CKV_E_INVALID;
   c->sched.reset();
+  for (int& n : c->text_len) n = 0;
   return CKV_OK;
 }
 
@@ -388,6 +396,64 @@ ckv_status ckv_chunk_attention(ckv_cache* c, int32_t layer, int32_t step, int32_
   p.part_o = (float*)(c->arena + c->L.part_o_off);
   p.part_lse = (float*)(c->arena + c->L.part_lse_off);
   if ((size_t)p.n_queries > c->L.scratch_queries) return CKV_E_INVALID;
+  return ckv::launch_chunk_attention(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
+}
+
+ckv_status ckv_text_store(ckv_cache* c, int32_t layer, const void* k_text, const void* v_text, int32_t n_text,
+                          void* stream) {
+  if (!c) return CKV_E_INVALID;
+  if (!ptr_ok(k_text) || !ptr_ok(v_text)) return CKV_E_INVALID;
+  if (layer < 0 || layer >= c->cfg.num_layers || n_text < 1 || n_text > CKV_MAX_TEXT_TOKENS) return CKV_E_INVALID;
+  if (!c->dry) {
+    hipStream_t s = (hipStream_t)stream;
+    ckv_status st = ensure_device(c, s);
+    if (st != CKV_OK) return st;
+    ckv::TextStoreParams p;
+    p.k = (const bf16_t*)k_text;
+    p.v = (const bf16_t*)v_text;
+    p.k_dst = c->text_k(layer);
+    p.vt_dst = c->text_vt(layer);
+    p.n_text = n_text;
+    p.max_text = CKV_MAX_TEXT_TOKENS;
+    p.num_heads = c->cfg.num_heads;
+    if (ckv::launch_text_store(p, c->cfg.head_dim, s) != hipSuccess) return CKV_E_HIP;
+  }
+  c->text_len[layer] = n_text;
+  return CKV_OK;
+}
+
+ckv_status ckv_cross_attention(ckv_cache* c, int32_t layer, int32_t chunk, const void* q, void* out, void* stream) {
+  if (!c) return CKV_E_INVALID;
+  if (!ptr_ok(q) || !ptr_ok(out)) return CKV_E_INVALID;
+  if (layer < 0 || layer >= c->cfg.num_layers || chunk < 0 || chunk >= c->cfg.max_chunks) return CKV_E_INVALID;
+  const int n_text = c->text_len[layer];
+  if (n_text == 0) return CKV_E_STATE;
+  if (c->dry) return CKV_OK;
+  hipStream_t s = (hipStream_t)stream;
+  ckv_status st = ensure_device(c, s);
+  if (st != CKV_OK) return st;
+  const long long d = c->cfg.head_dim;
+  ckv::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int i = 0; i < 3; ++i) {  // one run: the stored context
+    p.k[i] = c->text_k(layer);
+    p.vt[i] = c->text_vt(layer);
+    p.k_head_stride[i] = (long long)CKV_MAX_TEXT_TOKENS * d;
+    p.vt_head_stride[i] = d * CKV_MAX_TEXT_TOKENS;
+    p.vt_row_stride[i] = CKV_MAX_TEXT_TOKENS;
+    p.seg_end[i] = n_text;
+  }
+  p.q = (const bf16_t*)q;
+  p.out = (bf16_t*)out;
+  p.n_queries = c->tokens(chunk);
+  p.n_keys = n_text;
+  p.num_heads = c->cfg.num_heads;
+  p.n_splits = splits_for(c->num_cus, c->cfg.num_heads, p.n_queries, p.n_keys);
+  p.q_tiles = (p.n_queries + ckv::kAttnQueryTile - 1) / ckv::kAttnQueryTile;
+  p.key_tiles = (p.n_keys + ckv::kAttnKeyTile - 1) / ckv::kAttnKeyTile;
+  p.scale_log2 = c->scale() * 1.4426950408889634f;
+  p.part_o = (float*)(c->arena + c->L.part_o_off);
+  p.part_lse = (float*)(c->arena + c->L.part_lse_off);
   return ckv::launch_chunk_attention(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
 }
 

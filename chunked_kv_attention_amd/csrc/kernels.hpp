@@ -35,6 +35,16 @@ struct RopeAppendParams {
   float eps;
 };
 
+// The text context of one layer into the attention store: K rows
+// [H][max_text][d] and V^T [H][d][max_text], V^T columns past n_text zeroed.
+struct TextStoreParams {
+  const bf16_t* k;           // [n_text][H][d]
+  const bf16_t* v;           // [n_text][H][d]
+  bf16_t* k_dst;
+  bf16_t* vt_dst;
+  int n_text, max_text, num_heads;
+};
+
 // Up to three runs of keys, in key order; run r holds keys [end[r-1], end[r]).
 struct AttnParams {
   const bf16_t* q;           // [nq][H][d]
@@ -70,6 +80,7 @@ constexpr int kAttnQueryTile = 128;  // query rows per workgroup
 constexpr int kAttnKeyTile = 64;     // keys per LDS tile
 
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s);
+hipError_t launch_text_store(const TextStoreParams& p, int head_dim, hipStream_t s);
 hipError_t launch_chunk_attention(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_copy_kv(const CopyKVParams& p, int head_dim, hipStream_t s);
 

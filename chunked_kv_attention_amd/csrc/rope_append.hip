@@ -1,4 +1,5 @@
-// 3D RoPE + K/V append for one chunk, and the K/V copy-out used for checks.
+// 3D RoPE + K/V append for one chunk, the text-context store for
+// cross-attention, and the K/V copy-out used for checks.
 //
 // RoPE ("Learning Video Generation from the Wan2.2 Source Code", Chapter 4,
 // "3D RoPE"): the head dim is split into a time band of d - 4(d/6) dims and
@@ -221,6 +222,54 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeAppendParams 
   }
 }
 
+// The text context of one layer into the attention store.  Blocks
+// [0, k_blocks) copy K rows ([n][H][d] -> [H][max][d], 16 bytes a lane);
+// the rest write V^T for 64 context rows of one head through LDS, zero past
+// n_text so that every V^T column the attention reads is finite.
+template <int D>
+__global__ __launch_bounds__(kThreads) void text_store_kernel(TextStoreParams p, int k_blocks) {
+  constexpr int C8 = D / 8;
+  __shared__ uint16_t sv[kTok][D + 8];
+  const int H = p.num_heads;
+  if ((int)blockIdx.x < k_blocks) {
+    const long long e = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= (long long)p.n_text * H * C8) return;
+    const int c = (int)(e % C8);
+    const long long th = e / C8;
+    const int head = (int)(th % H);
+    const int tok = (int)(th / H);
+    *reinterpret_cast<uint4*>(p.k_dst + ((long long)head * p.max_text + tok) * D + c * 8) =
+        *reinterpret_cast<const uint4*>(p.k + e * 8);
+    return;
+  }
+  const int vb = blockIdx.x - k_blocks;
+  const int head = vb / (p.max_text / kTok);
+  const int tok0 = (vb % (p.max_text / kTok)) * kTok;
+#pragma unroll
+  for (int it = 0; it < (kTok * C8) / kThreads; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    const int t = idx / C8;
+    const int c = idx % C8;
+    const int tok = tok0 + t;
+    *reinterpret_cast<uint4*>(&sv[t][c * 8]) =
+        tok < p.n_text ? *reinterpret_cast<const uint4*>(p.v + ((long long)tok * H + head) * D + c * 8)
+                       : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < (kTok / 8 * D) / kThreads; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    const int g = idx % (kTok / 8);
+    const int dim = idx / (kTok / 8);
+    const int t = g * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)sv[t + 2 * j][dim] | ((uint32_t)sv[t + 2 * j + 1][dim] << 16);
+    *reinterpret_cast<uint4*>(p.vt_dst + ((long long)head * D + dim) * p.max_text + tok0 + t) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void copy_kv_kernel(CopyKVParams p) {
   const long long total = (long long)p.n_tokens * p.num_heads * D;
@@ -250,6 +299,20 @@ hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream
     hipLaunchKernelGGL((rope_append_kernel<64, true>), grid, dim3(kThreads), 0, s, p, qk_blocks);
   else if (head_dim == 64)
     hipLaunchKernelGGL((rope_append_kernel<64, false>), grid, dim3(kThreads), 0, s, p, qk_blocks);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_text_store(const TextStoreParams& p, int head_dim, hipStream_t s) {
+  if (p.n_text <= 0 || p.n_text > p.max_text || p.max_text % kTok != 0 || p.num_heads <= 0) return hipErrorInvalidValue;
+  const long long chunks = (long long)p.n_text * p.num_heads * (head_dim / 8);
+  const int k_blocks = (int)((chunks + kThreads - 1) / kThreads);
+  const dim3 grid(k_blocks + p.num_heads * (p.max_text / kTok));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(text_store_kernel<128>, grid, dim3(kThreads), 0, s, p, k_blocks);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(text_store_kernel<64>, grid, dim3(kThreads), 0, s, p, k_blocks);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

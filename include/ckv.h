@@ -57,6 +57,11 @@ typedef enum ckv_status {
 /* Step id of the first chunk's extra clean (sigma = 0) pass. */
 #define CKV_STEP_SINK (-1)
 
+/* Longest text context a layer stores ("Learning Video Generation from the
+ * Wan2.2 Source Code", Chapter 3, "Where Did the Prompt Go?": the prompt
+ * becomes up to 512 context vectors). */
+#define CKV_MAX_TEXT_TOKENS 512
+
 /* Model and schedule.  Layout is fixed (56 bytes) for foreign-function use. */
 typedef struct ckv_config {
   int32_t num_layers;         /* caches kept per layer (e.g. 30)                      */
@@ -172,6 +177,28 @@ ckv_status ckv_norm_sink_build(ckv_cache* c, int32_t layer, const void* q, const
  * out is [n_tokens][H][d] bf16.  The softmax is accumulated in fp32. */
 ckv_status ckv_chunk_attention(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk,
                                const void* q_rot, void* out, void* stream);
+
+/* Store one layer's text context for cross-attention ("Learning Video
+ * Generation from the Wan2.2 Source Code", Chapter 3, "Where Did the Prompt
+ * Go?": the context, trimmed to the prompt's real length, is the key/value of
+ * every layer's cross-attention and never changes during a rollout).
+ * k_text, v_text: [n_text][H][d] bf16 device tensors, the layer's projected
+ * context keys and values (no rotation), read during the call.
+ * 1 <= n_text <= CKV_MAX_TEXT_TOKENS, 0 <= layer < num_layers (else
+ * CKV_E_INVALID).  Replaces any context stored for the layer; cleared by
+ * ckv_cache_reset.  The arena holds one context per layer
+ * (ckv_cache_bytes includes it). */
+ckv_status ckv_text_store(ckv_cache* c, int32_t layer, const void* k_text, const void* v_text,
+                          int32_t n_text, void* stream);
+
+/* Cross-attention of one chunk's video tokens to the layer's stored context
+ * (same chapter; the block's cross-attention takes the video tokens as
+ * queries): out = softmax(scale * q K_text^T) V_text per head over the n_text
+ * stored rows, no mask, no rotation.  q and out are [tokens(chunk)][H][d]
+ * bf16 (2640 rows for chunk 0, h*w per later chunk).  CKV_E_STATE if the
+ * layer has no context; independent of the ring schedule. */
+ckv_status ckv_cross_attention(ckv_cache* c, int32_t layer, int32_t chunk, const void* q,
+                               void* out, void* stream);
 
 /* Host-only: the window (layer, step, chunk) attends to, as <= 3 segments in
  * key order (sink area, then up to two runs of ring slots; the last run ends

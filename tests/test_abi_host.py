@@ -38,7 +38,7 @@ def test_status_strings():
 def test_cache_bytes_covers_store():
     n1, n0, R = 880, 2640, 19
     H, d, L, S = 24, 128, 2, 4
-    store = L * 2 * H * n0 * d * 2 + L * S * 2 * H * R * n1 * d * 2
+    store = L * 2 * H * n0 * d * 2 + L * S * 2 * H * R * n1 * d * 2 + L * 2 * H * C.MAX_TEXT_TOKENS * d * 2
     nbytes = C.cache_bytes(PROFILE)
     assert store <= nbytes <= store + 4 * n0 * H * (d + 1) * 4 + (1 << 20)
     bad = [dict(head_dim=96), dict(grid_w=41), dict(num_layers=0), dict(window_chunks=-1),
@@ -219,3 +219,35 @@ def test_norm_entry_points_validate_and_follow_the_schedule():
     cache.norm_rope_append(0, 0, 1, *a, *g, 1e-6, FAKE)
     cache.rope_append(0, 0, 2, *a, FAKE)  # plain and norm appends share one ring order
     cache.chunk_attention(0, 0, 2, FAKE, FAKE)
+
+
+def test_text_context_store_and_cross_attention_rules():
+    cache = C.Cache(TINY, dry=True)
+    # no context yet
+    _expect(C.CKV_E_STATE, cache.cross_attention, 0, 1, FAKE, FAKE)
+    # argument checks
+    for n in (0, -1, C.MAX_TEXT_TOKENS + 1):
+        _expect(C.CKV_E_INVALID, cache.text_store_rows, 0, FAKE, FAKE, n)
+    _expect(C.CKV_E_INVALID, cache.text_store_rows, 1, FAKE, FAKE, 8)       # one layer only
+    _expect(C.CKV_E_INVALID, cache.text_store_rows, 0, 0, FAKE, 8)          # null
+    _expect(C.CKV_E_INVALID, cache.text_store_rows, 0, FAKE + 8, FAKE, 8)   # misaligned
+    cache.text_store_rows(0, FAKE, FAKE, 77)
+    cache.text_store_rows(0, FAKE, FAKE, C.MAX_TEXT_TOKENS)  # replaces
+    # independent of the ring schedule: any chunk index, before any append
+    cache.cross_attention(0, 0, FAKE, FAKE)
+    cache.cross_attention(0, 5, FAKE, FAKE)
+    _expect(C.CKV_E_INVALID, cache.cross_attention, 0, 6, FAKE, FAKE)
+    _expect(C.CKV_E_INVALID, cache.cross_attention, 1, 1, FAKE, FAKE)
+    cache.reset()  # a new rollout (prompt) forgets the context
+    _expect(C.CKV_E_STATE, cache.cross_attention, 0, 1, FAKE, FAKE)
+
+
+def test_cache_bytes_include_one_context_per_layer():
+    one = C.cache_bytes(PROFILE)
+    more = C.cache_bytes(C.Config(num_layers=PROFILE.num_layers + 1, num_steps=4, num_heads=24, head_dim=128, grid_h=22, grid_w=40,
+                                  first_chunk_frames=3, window_chunks=18, max_chunks=29))
+    # per layer: sink + 4 rings + the context's K and V^T (512 x 24 x 128 bf16 each)
+    sink = 2 * 24 * 2640 * 128 * 2
+    rings = 4 * 2 * 24 * 19 * 880 * 128 * 2
+    text = 2 * 24 * 512 * 128 * 2
+    assert more - one == sink + rings + text
