@@ -14,10 +14,14 @@ whole rollout (4 * n_q * n_k * 3072 per attention call, the convention of
 dominant kernel, chunk attention (the MFMA kernel plus, when the key range is
 split, its small merge kernel), over all of its launches in the timed
 rollouts, timed with HIP events on the launch stream; the 880-query x
-19,360-key launches (chunks 19..28) are also reported on their own.
+19,360-key launches (chunks 19..28) are also reported on their own.  After
+the timed rollouts (outside them) it also reports the QK-Norm + RoPE + append
+path, a device copy of the append's byte count, and the cross-attention of an
+880-token chunk to a 512-row text context; `--no-extras` skips these, so that
+a profiled run traces only the rollout's launches.
 
 `--counters FETCH.csv WRITE.csv` turns two rocprofv3 --pmc runs of
-`bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration` (one for
+`bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras --copy-calibration` (one for
 FETCH_SIZE, one for WRITE_SIZE) into the HBM traffic per chunk-attention
 call, scaled by what the same counters read for the plain 1 GiB copy, and
 writes it with the kernel source's hash to profiles/.
@@ -53,6 +57,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the QK-Norm append, cross-attention and copy lines (profiling runs: only the "
+                         "rollout's launches are traced)")
     ap.add_argument("--workload", choices=["rollout1", "rollout30x2"], default="rollout1",
                     help="rollout1: 1-layer 29-chunk rollout (default); rollout30x2: 30 layers x 2 prompts on "
                          "2 streams")
@@ -143,9 +150,9 @@ def summarise_counters(fetch_csv, write_csv):
         "# averaged over the 117 calls of one 1-layer 29-chunk rollout.",
         "# Commands (run from the repository root; cd /tmp && export TMPDIR=/tmp first):",
         "#   rocprofv3 --pmc FETCH_SIZE -d OUT_F -o fetch --output-format csv -- "
-        "python bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+        "python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras --copy-calibration",
         "#   rocprofv3 --pmc WRITE_SIZE -d OUT_W -o write --output-format csv -- "
-        "python bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+        "python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras --copy-calibration",
         "#   python bench.py --counters OUT_F/fetch_counter_collection.csv OUT_W/write_counter_collection.csv",
         "# Scaling: the same counters read for the plain 1 GiB device copy (reads and writes 1 GiB).",
         f"copy_fetch_kib = {big_copy_f:.0f}",
@@ -526,9 +533,10 @@ def main():
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         },
     }
-    result["norm_rope_append_880"], result["device_copy_same_bytes"] = norm_append_and_copy(
-        C, cfg, dev, stream, inputs, calls)
-    result["cross_attn_880x512"] = cross_attention_timing(C, cfg, dev, stream)
+    if not args.no_extras:
+        result["norm_rope_append_880"], result["device_copy_same_bytes"] = norm_append_and_copy(
+            C, cfg, dev, stream, inputs, calls)
+        result["cross_attn_880x512"] = cross_attention_timing(C, cfg, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
     print(json.dumps(result), flush=True)
