@@ -20,6 +20,10 @@ path, a device copy of the append's byte count, and the cross-attention of an
 880-token chunk to a 512-row text context; `--no-extras` skips these, so that
 a profiled run traces only the rollout's launches.
 
+`--workload rollout30x2` times the whole model's attention traffic (30 layers
+x 2 prompts on 2 streams); `--workload attn880x19360` times the chunk-19
+attention call alone, for per-kernel counter runs.
+
 `--counters FETCH.csv WRITE.csv` turns two rocprofv3 --pmc runs of
 `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras --copy-calibration` (one for
 FETCH_SIZE, one for WRITE_SIZE) into the HBM traffic per chunk-attention
@@ -60,9 +64,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the QK-Norm append, cross-attention and copy lines (profiling runs: only the "
                          "rollout's launches are traced)")
-    ap.add_argument("--workload", choices=["rollout1", "rollout30x2"], default="rollout1",
+    ap.add_argument("--workload", choices=["rollout1", "rollout30x2", "attn880x19360"], default="rollout1",
                     help="rollout1: 1-layer 29-chunk rollout (default); rollout30x2: 30 layers x 2 prompts on "
-                         "2 streams")
+                         "2 streams; attn880x19360: the chunk-19 attention call alone, --steps times (for "
+                         "per-kernel counter runs)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the counters file and exit")
     return ap.parse_args()
@@ -305,6 +310,63 @@ def rollout30x2(args):
     print(json.dumps(result), flush=True)
 
 
+def attn880x19360(args):
+    """The 880-query x 19,360-key chunk-attention call on its own: a 1-layer
+    cache filled with the sink and chunks 1..19 at step 0 (seeded N(0,1)
+    inputs), then `--steps` timed calls of chunk 19's attention after
+    `--warmup` untimed ones.  Used for per-kernel counter runs, where the
+    rollout's mix of call shapes would blur the counters."""
+    import torch
+
+    import chunked_kv_attention_amd as C
+
+    cfg = profile_config()
+    H, d = cfg.num_heads, cfg.head_dim
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+
+    def rnd(n):
+        return torch.randn((n, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    cache = C.Cache(cfg)
+    n0, n1 = cfg.tokens(0), cfg.tokens(1)
+    q0 = rnd(n0)
+    cache.sink_build(0, q0, rnd(n0), rnd(n0), torch.empty_like(q0))
+    q_rot = torch.empty((n1, H, d), device=dev, dtype=torch.bfloat16)
+    for c in range(1, 20):
+        cache.rope_append(0, 0, c, rnd(n1), rnd(n1), rnd(n1), q_rot)
+    out = torch.empty_like(q_rot)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        cache.chunk_attention(0, 0, 19, q_rot, out, stream=stream)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        cache.chunk_attention(0, 0, 19, q_rot, out, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * start.elapsed_time(stop) / args.steps
+    flops = attn_flops(cfg, 19)
+    tflops = flops / (us * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "chunk-attn TFLOP/s, 880 queries x 19,360 keys",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "us_per_call": round(us, 2),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "one chunk-attention call: 880 queries x 19,360 keys (sink + 18 chunks + self), "
+                               "24 heads x 128", "key_splits": cache.attention_splits(n1, 19360)},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+    }), flush=True)
+
+
 def norm_append_and_copy(C, cfg, dev, stream, inputs, calls):
     """QK-Norm + RoPE + append on the 880-token chunks (its own cache; gains
     seeded), and a plain device copy of the same byte count for context."""
@@ -402,6 +464,9 @@ def main():
     C.load()
     if args.workload == "rollout30x2":
         rollout30x2(args)
+        return
+    if args.workload == "attn880x19360":
+        attn880x19360(args)
         return
     dev = torch.device("cuda:0")
     cfg = profile_config()

@@ -24,7 +24,6 @@
 // wave
 //   S^T[64 keys x 32 queries] = K_tile Q^T      8 independent 16x16 blocks
 //   O^T[d x 32 queries]      += V^T_tile P^T    2d/16 independent blocks
-//   l[32 queries]            += 1 P^T           row sums, 4 more MFMAs
 // so both products keep many accumulation chains in flight.  With the
 // queries as the N columns, a lane holds 16 scores of each of its 2 queries;
 // a query's row max needs a 4-lane exchange (lane xor 16, xor 32).  K rows
@@ -36,8 +35,11 @@
 // per score before exp2.  The running max is lazy: O and the running sums are
 // rescaled only when a tile raises some row's max by more than 2^8 (a
 // wave-uniform branch), otherwise the stale max is kept and P may reach 256,
-// which bf16 and the fp32 accumulators hold exactly enough.  The row sums are
-// taken on the matrix unit from the same bf16-rounded P that multiplies V, so
+// which bf16 and the fp32 accumulators hold exactly enough.  The test needs
+// no cross-lane max: each lane compares its own raw scores of a query with
+// that query's threshold (m + 8) / (scale log2 e), and the 4-lane max is
+// taken only inside the rare rescale branch.  The row sums add the same
+// bf16-rounded P that multiplies V (v_dot2_f32_bf16 against ones), so
 // numerator and denominator see the same weights.
 //
 // Occupancy.  880 queries x 24 heads is only 168 workgroups of 128 rows for
@@ -109,6 +111,26 @@ __device__ inline float quad_max(float x) {
   x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
+// max of finite floats without the quieting of NaN inputs that fmaxf implies
+__device__ inline float max3f(float a, float b, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+#else
+  return fmaxf(a, fmaxf(b, c));
+#endif
+}
+__device__ inline float max2f(float a, float b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+#else
+  return fmaxf(a, b);
+#endif
 }
 
 // The up to three runs of this head's window, loaded once into uniform
@@ -286,7 +308,7 @@ __device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, 
 template <int D>
 __device__ inline void attend_tile(const char* sk, const char* sv, const int (&ka)[D / 32], const int (&va)[KS],
                                    const bf16x8 (&qf)[D / 32][2], f32x4 (&o)[D / 16][2], float (&m)[2],
-                                   float (&lsum)[2], float scale_log2, bool masked, int t0, int key_end, int h) {
+                                   float (&thr)[2], float (&lsum)[2], float scale_log2, bool masked, int t0, int key_end, int h) {
   using T = Tile<D>;
   constexpr int KK = D / 32;
   constexpr int DB = D / 16;
@@ -322,25 +344,32 @@ __device__ inline void attend_tile(const char* sk, const char* sv, const int (&k
         for (int i = 0; i < 4; ++i)
           if (t0 + 32 * (kb / 2) + 8 * h + 4 * (kb % 2) + i >= key_end) s[kb][qb][i] = -INFINITY;
   }
-  float mt[2];
+  // Rescale test without the cross-lane max: a query needs a new max only if
+  // one of its raw scores exceeds thr = (m + 2^8 headroom) / scale_log2, and
+  // every lane can test its own 16 scores of each query.  The 4-lane max is
+  // taken only in the rare branch.
+  float lm[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float mx = s[0][qb][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-    mt[qb] = quad_max(mx) * scale_log2;
+    float a = max3f(s[0][qb][0], s[0][qb][1], s[0][qb][2]);
+    float b = max3f(s[0][qb][3], s[1][qb][0], s[1][qb][1]);
+    float c = max3f(s[1][qb][2], s[1][qb][3], s[2][qb][0]);
+    float d = max3f(s[2][qb][1], s[2][qb][2], s[2][qb][3]);
+    float e = max3f(s[3][qb][0], s[3][qb][1], s[3][qb][2]);
+    a = max3f(a, b, s[3][qb][3]);
+    c = max3f(c, d, e);
+    lm[qb] = max2f(a, c);
   }
-  if (__any(mt[0] > m[0] + kRescaleLog2 || mt[1] > m[1] + kRescaleLog2)) {
+  if (__any(lm[0] > thr[0] || lm[1] > thr[1])) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float m_new = fmaxf(m[qb], mt[qb]);
+      const float m_new = fmaxf(m[qb], quad_max(lm[qb]) * scale_log2);
       const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
       lsum[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
       m[qb] = m_new;
+      thr[qb] = (m_new + kRescaleLog2) / scale_log2;
     }
   }
 
@@ -439,6 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
     for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY};  // running max of scaled scores (log2 domain), per query block
   float lsum[2] = {0.f, 0.f};  // this lane's share of the running sums
+  float thr[2] = {-INFINITY, -INFINITY};  // raw-score level that forces a rescale
 
   fetch_tile<D>(runs, slots, cursor, wave, lane, t_begin * KT, key_begin, key_end, sk0, sv0);
   for (int t = t_begin; t < t_end; t += 2) {
@@ -446,12 +476,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 1 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 1) * KT, key_begin, key_end, sk1, sv1);
-    attend_tile<D>(sk0, sv0, ka, va, qf, o, m, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
+    attend_tile<D>(sk0, sv0, ka, va, qf, o, m, thr, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
     if (t + 1 >= t_end) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 2 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 2) * KT, key_begin, key_end, sk0, sv0);
-    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT, key_end,
+    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, thr, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT, key_end,
                    h);
   }
 
