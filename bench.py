@@ -22,7 +22,9 @@ a profiled run traces only the rollout's launches.
 
 `--workload rollout30x2` times the whole model's attention traffic (30 layers
 x 2 prompts on 2 streams); `--workload attn880x19360` times the chunk-19
-attention call alone, for per-kernel counter runs.
+attention call alone, for per-kernel counter runs; `--workload
+conv88x160x384` / `conv44x80x384` time one streaming causal Conv3d layer of
+the VAE decoder (also reported as extras of the default line).
 
 `--counters FETCH.csv WRITE.csv` turns two rocprofv3 --pmc runs of
 `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras --copy-calibration` (one for
@@ -64,10 +66,12 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the QK-Norm append, cross-attention and copy lines (profiling runs: only the "
                          "rollout's launches are traced)")
-    ap.add_argument("--workload", choices=["rollout1", "rollout30x2", "attn880x19360"], default="rollout1",
+    ap.add_argument("--workload", choices=["rollout1", "rollout30x2", "attn880x19360", "conv88x160x384",
+                                           "conv44x80x384"], default="rollout1",
                     help="rollout1: 1-layer 29-chunk rollout (default); rollout30x2: 30 layers x 2 prompts on "
                          "2 streams; attn880x19360: the chunk-19 attention call alone, --steps times (for "
-                         "per-kernel counter runs)")
+                         "per-kernel counter runs); conv88x160x384 / conv44x80x384: one streaming causal Conv3d "
+                         "layer of the VAE decoder alone")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the counters file and exit")
     return ap.parse_args()
@@ -445,6 +449,63 @@ def cross_attention_timing(C, cfg, dev, stream):
             "key_splits": cache.attention_splits(880, 512)}
 
 
+CONV_LAYERS = {
+    # name: (H, W, C_in, C_out, frames per call) -- 3x3x3 causal Conv3d layers
+    "conv88x160x384": (88, 160, 384, 384, 2),
+    "conv44x80x384": (44, 80, 384, 384, 1),
+}
+
+
+def conv_timing(name, calls=40, warmup=4):
+    """Streaming causal Conv3d through the C-ABI: `calls` chunks of one layer
+    (seeded N(0,1) bf16 frames, weights N(0,1)/sqrt(fan-in)), event-timed on
+    the launch stream; each call is the conv kernel plus the cache update.
+    FLOPs = 2 * pixels * C_out * 27 * C_in per call."""
+    import torch
+
+    import chunked_kv_attention_amd as C
+
+    h, w, ci, co, frames = CONV_LAYERS[name]
+    cfg = C.ConvConfig(height=h, width=w, in_channels=ci, out_channels=co, max_frames=frames)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+    weight = (torch.randn((co, ci, 3, 3, 3), generator=g, device=dev) / (27 * ci) ** 0.5).to(torch.bfloat16)
+    bias = (0.1 * torch.randn((co,), generator=g, device=dev)).to(torch.bfloat16)
+    xs = [torch.randn((frames, h, w, ci), generator=g, device=dev).to(torch.bfloat16) for _ in range(4)]
+    y = torch.empty((frames, h, w, co), device=dev, dtype=torch.bfloat16)
+    state = C.CausalConv(cfg)
+    stream = torch.cuda.current_stream()
+    state.set_weights(weight, bias, stream=stream)
+    for i in range(warmup):
+        state(xs[i % 4], y, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(calls):
+        state(xs[i % 4], y, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    flops = 2 * frames * h * w * co * 27 * ci
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"us_per_call": round(us, 2), "tflops": round(tflops, 2),
+            "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "gflop_per_call": round(flops / 1e9, 2),
+            "layer": f"causal Conv3d 3x3x3, {ci}->{co} channels, {h}x{w} grid, {frames} frame(s) per call",
+            "calls_timed": calls}
+
+
+def conv_workload(args):
+    """`--workload conv88x160x384` / `conv44x80x384`: one streaming causal
+    Conv3d layer alone, `--steps` timed calls (for per-kernel profiles)."""
+    r = conv_timing(args.workload, calls=args.steps, warmup=args.warmup)
+    print(json.dumps({
+        "metric": "streaming causal Conv3d TFLOP/s", "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "us_per_call": r["us_per_call"], "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic", "config": {"workload": r["layer"]},
+        "pct_bf16_peak": r["pct_bf16_peak"],
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.counters:
@@ -467,6 +528,9 @@ def main():
         return
     if args.workload == "attn880x19360":
         attn880x19360(args)
+        return
+    if args.workload in CONV_LAYERS:
+        conv_workload(args)
         return
     dev = torch.device("cuda:0")
     cfg = profile_config()
@@ -602,6 +666,8 @@ def main():
         result["norm_rope_append_880"], result["device_copy_same_bytes"] = norm_append_and_copy(
             C, cfg, dev, stream, inputs, calls)
         result["cross_attn_880x512"] = cross_attention_timing(C, cfg, dev, stream)
+        result["causal_conv_88x160x384"] = conv_timing("conv88x160x384")
+        result["causal_conv_44x80x384"] = conv_timing("conv44x80x384")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
     print(json.dumps(result), flush=True)

@@ -1,4 +1,5 @@
-"""ctypes binding of libckv.so (include/ckv.h): argument marshalling only.
+"""ctypes binding of libckv.so (include/ckv.h, include/ckv_conv.h): argument
+marshalling only.
 
 Every operation runs in the HIP library; this module checks tensor shapes and
 dtypes, passes device pointers and the current HIP stream, and turns status
@@ -17,13 +18,17 @@ CKV_OK, CKV_E_INVALID, CKV_E_ORDER, CKV_E_STATE, CKV_E_ARENA, CKV_E_HIP = range(
 STEP_SINK = -1
 MAX_TEXT_TOKENS = 512
 
-# Every symbol include/ckv.h declares.
+CONV_CACHE_T = 2
+
+# Every symbol include/*.h declares.
 EXPORTS = (
     "ckv_cache_bytes", "ckv_cache_create", "ckv_cache_create_dry", "ckv_cache_reset",
     "ckv_cache_destroy", "ckv_rope_append", "ckv_sink_build", "ckv_norm_rope_append",
     "ckv_norm_sink_build", "ckv_chunk_attention", "ckv_text_store", "ckv_cross_attention",
     "ckv_window", "ckv_ring_slot", "ckv_debug_copy_kv", "ckv_attention_splits",
     "ckv_status_string",
+    "ckv_conv_bytes", "ckv_conv_create", "ckv_conv_create_dry", "ckv_conv_set_weights", "ckv_conv_reset",
+    "ckv_causal_conv", "ckv_conv_position", "ckv_conv_destroy",
 )
 
 
@@ -46,6 +51,11 @@ class CkvConfig(ctypes.Structure):
 
 
 assert ctypes.sizeof(CkvConfig) == 56
+
+
+class CkvConvConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("height", "width", "in_channels", "out_channels", "kt", "kh", "kw",
+                                              "max_frames")]
 
 
 class CkvSegment(ctypes.Structure):
@@ -89,6 +99,14 @@ def load() -> ctypes.CDLL:
         "ckv_debug_copy_kv": (I32, [P, I32, I32, I32, P, P, P]),
         "ckv_attention_splits": (I32, [P, I32, I32]),
         "ckv_status_string": (ctypes.c_char_p, [I32]),
+        "ckv_conv_bytes": (SZ, [ctypes.POINTER(CkvConvConfig)]),
+        "ckv_conv_create": (I32, [ctypes.POINTER(CkvConvConfig), P, SZ, ctypes.POINTER(P)]),
+        "ckv_conv_create_dry": (I32, [ctypes.POINTER(CkvConvConfig), ctypes.POINTER(P)]),
+        "ckv_conv_set_weights": (I32, [P, P, P, P]),
+        "ckv_conv_reset": (I32, [P]),
+        "ckv_causal_conv": (I32, [P, P, I32, P, P]),
+        "ckv_conv_position": (ctypes.c_int64, [P]),
+        "ckv_conv_destroy": (I32, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -273,6 +291,118 @@ class Cache:
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
             self._lib.ckv_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+@dataclass(frozen=True)
+class ConvConfig:
+    """One causal Conv3d layer (include/ckv_conv.h): grid, channels, kernel,
+    largest chunk."""
+    height: int
+    width: int
+    in_channels: int
+    out_channels: int
+    kt: int = 3
+    kh: int = 3
+    kw: int = 3
+    max_frames: int = 1
+
+    def to_c(self) -> CkvConvConfig:
+        return CkvConvConfig(self.height, self.width, self.in_channels, self.out_channels, self.kt, self.kh, self.kw,
+                             self.max_frames)
+
+    @property
+    def taps(self) -> int:
+        return self.kt * self.kh * self.kw
+
+
+def conv_bytes(cfg: ConvConfig) -> int:
+    c = cfg.to_c()
+    return int(load().ckv_conv_bytes(ctypes.byref(c)))
+
+
+class CausalConv:
+    """Streaming causal Conv3d state (packed weights, bias, 2-frame cache)
+    over a torch arena.  `dry=True` makes a host-only state whose calls
+    validate and advance the position without a device; pointers may then be
+    any 16-byte aligned integers."""
+
+    def __init__(self, cfg: ConvConfig, dry: bool = False, device=None):
+        self.cfg = cfg
+        self.dry = dry
+        self._lib = load()
+        self._c = cfg.to_c()
+        h = ctypes.c_void_p()
+        if dry:
+            self.arena = None
+            _check(self._lib.ckv_conv_create_dry(ctypes.byref(self._c), ctypes.byref(h)), "ckv_conv_create_dry")
+        else:
+            import torch
+            nbytes = self._lib.ckv_conv_bytes(ctypes.byref(self._c))
+            if nbytes == 0:
+                raise CkvError(CKV_E_INVALID, "ckv_conv_bytes")
+            self.arena = torch.empty(int(nbytes), dtype=torch.uint8, device=device or "cuda")
+            _check(self._lib.ckv_conv_create(ctypes.byref(self._c), self.arena.data_ptr(), int(nbytes),
+                                             ctypes.byref(h)), "ckv_conv_create")
+        self._h = h
+
+    def _ptr(self, t, shape, name, optional=False):
+        if t is None and optional:
+            return None
+        if self.dry and isinstance(t, int):
+            return t
+        import torch
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 device tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        return t.data_ptr()
+
+    def _stream(self, stream):
+        if self.dry:
+            return None
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        return s.cuda_stream
+
+    def set_weights(self, weight, bias=None, stream=None):
+        """weight [C_out][C_in][kt][kh][kw] bf16 (Conv3d's layout), bias [C_out] bf16 or None."""
+        c = self.cfg
+        wp = self._ptr(weight, (c.out_channels, c.in_channels, c.kt, c.kh, c.kw), "weight")
+        bp = self._ptr(bias, (c.out_channels,), "bias", optional=True)
+        _check(self._lib.ckv_conv_set_weights(self._h, wp, bp, self._stream(stream)), "ckv_conv_set_weights")
+
+    def __call__(self, x, y, stream=None):
+        """x [frames][H][W][C_in] -> y [frames][H][W][C_out] (bf16, channels last)."""
+        c = self.cfg
+        frames = int(x.shape[0])
+        xp = self._ptr(x, (frames, c.height, c.width, c.in_channels), "x")
+        yp = self._ptr(y, (frames, c.height, c.width, c.out_channels), "y")
+        _check(self._lib.ckv_causal_conv(self._h, xp, frames, yp, self._stream(stream)), "ckv_causal_conv")
+
+    def call_raw(self, x_ptr, frames, y_ptr, stream=None):
+        """Raw-pointer form (dry states and tests of the argument checks)."""
+        _check(self._lib.ckv_causal_conv(self._h, x_ptr, frames, y_ptr, self._stream(stream)), "ckv_causal_conv")
+
+    def set_weights_raw(self, w_ptr, b_ptr=None, stream=None):
+        _check(self._lib.ckv_conv_set_weights(self._h, w_ptr, b_ptr, self._stream(stream)), "ckv_conv_set_weights")
+
+    @property
+    def position(self) -> int:
+        return int(self._lib.ckv_conv_position(self._h))
+
+    def reset(self):
+        _check(self._lib.ckv_conv_reset(self._h), "ckv_conv_reset")
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.ckv_conv_destroy(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):

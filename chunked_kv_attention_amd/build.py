@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libckv.so")
-SOURCES = ["ckv_api.cpp", "rope_append.hip", "chunk_attn.hip"]
+SOURCES = ["ckv_api.cpp", "conv_api.cpp", "rope_append.hip", "chunk_attn.hip", "causal_conv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -76,6 +76,33 @@ struct CopyKVParams {
   bf16_t* v_out;        // [n][H][d]
 };
 
+// Streaming causal 3D convolution of one chunk (implicit GEMM).  Tap order
+// is Conv3d's (a, b, c) over (kt, kh, kw), a slowest.
+struct ConvParams {
+  const bf16_t* x;           // [frames][H][W][C_in]
+  bf16_t* y;                 // [frames][H][W][C_out]
+  const bf16_t* w;           // packed [taps][C_out][C_in]
+  const float* bias;         // [C_out]
+  bf16_t* cache;             // [2][H][W][C_in]: global frame g in slot g mod 2
+  const bf16_t* zero;        // >= C_in zeros (source of out-of-video taps)
+  long long k0;              // global index of the chunk's first frame
+  int frames, height, width, c_in, c_out, kt, kh, kw;
+  int m_tiles;               // ceil(frames * H * W / kConvPixelTile)
+};
+
+// Weights [C_out][C_in][taps] -> [taps][C_out][C_in], bias bf16 -> float32.
+struct ConvPackParams {
+  const bf16_t* weight;
+  const bf16_t* bias;        // or null (zero bias)
+  bf16_t* w_packed;
+  float* bias_out;
+  bf16_t* zero;              // zero_u4 16-byte units set to 0
+  int c_out, c_in, taps, zero_u4;
+};
+
+constexpr int kConvPixelTile = 128;    // output pixels per workgroup
+constexpr int kConvChannelTile = 128;  // output channels per workgroup
+
 constexpr int kAttnQueryTile = 128;  // query rows per workgroup
 constexpr int kAttnKeyTile = 64;     // keys per LDS tile
 
@@ -83,5 +110,7 @@ hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream
 hipError_t launch_text_store(const TextStoreParams& p, int head_dim, hipStream_t s);
 hipError_t launch_chunk_attention(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_copy_kv(const CopyKVParams& p, int head_dim, hipStream_t s);
+hipError_t launch_causal_conv(const ConvParams& p, hipStream_t s);
+hipError_t launch_conv_pack(const ConvPackParams& p, hipStream_t s);
 
 }  // namespace ckv

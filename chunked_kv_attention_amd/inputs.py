@@ -16,6 +16,7 @@ from __future__ import annotations
 import numpy as np
 
 TENSOR_CODES = {"q": 0, "k": 1, "v": 2}
+CONV_TENSOR_CODES = {"x": 3, "weight": 4, "bias": 5}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -57,3 +58,11 @@ def peaky_key_rows(total_keys: int, fraction: float, seed_key) -> np.ndarray:
     count = int(round(fraction * total_keys))
     rng = np.random.default_rng(np.random.SeedSequence([int(x) for x in seed_key]))
     return np.sort(rng.permutation(total_keys)[:count])
+
+
+def draw_conv_bits(shape, *, base_seed=0, layer=0, chunk=0, tensor="x", scale=1.0) -> np.ndarray:
+    """bf16 bit patterns of a causal-convolution input: N(0,1) times `scale`
+    (weights are drawn with scale 1/sqrt(fan-in) so outputs stay O(1)), keyed
+    by (base_seed, layer, chunk, tensor) like the attention inputs."""
+    key = (base_seed, 0, layer, chunk, 0, CONV_TENSOR_CODES[tensor])
+    return f32_to_bf16_bits(normal_f32(shape, key) * np.float32(scale))

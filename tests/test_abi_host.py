@@ -21,8 +21,11 @@ FAKE = 0x10000  # aligned, never dereferenced by a dry cache
 
 
 def test_exports_match_header():
-    header = open(os.path.join(ROOT, "include", "ckv.h")).read()
-    declared = set(re.findall(r"^(?:[\w\s\*]+?)\b(ckv_\w+)\s*\(", header, flags=re.M))
+    declared = set()
+    for name in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if name.endswith(".h"):
+            header = open(os.path.join(ROOT, "include", name)).read()
+            declared |= set(re.findall(r"^(?:[\w\s\*]+?)\b(ckv_\w+)\s*\(", header, flags=re.M))
     assert declared == set(C.EXPORTS)
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared:
