@@ -28,7 +28,7 @@ EXPORTS = (
     "ckv_window", "ckv_ring_slot", "ckv_debug_copy_kv", "ckv_attention_splits",
     "ckv_status_string",
     "ckv_conv_bytes", "ckv_conv_create", "ckv_conv_create_dry", "ckv_conv_set_weights", "ckv_conv_reset",
-    "ckv_causal_conv", "ckv_conv_position", "ckv_conv_destroy",
+    "ckv_causal_conv", "ckv_conv_position", "ckv_conv_splits", "ckv_conv_destroy",
 )
 
 
@@ -106,6 +106,7 @@ def load() -> ctypes.CDLL:
         "ckv_conv_reset": (I32, [P]),
         "ckv_causal_conv": (I32, [P, P, I32, P, P]),
         "ckv_conv_position": (ctypes.c_int64, [P]),
+        "ckv_conv_splits": (I32, [P, I32]),
         "ckv_conv_destroy": (I32, [P]),
     }
     for name, (res, args) in sig.items():
@@ -396,6 +397,9 @@ class CausalConv:
     @property
     def position(self) -> int:
         return int(self._lib.ckv_conv_position(self._h))
+
+    def splits(self, frames: int) -> int:
+        return int(self._lib.ckv_conv_splits(self._h, int(frames)))
 
     def reset(self):
         _check(self._lib.ckv_conv_reset(self._h), "ckv_conv_reset")

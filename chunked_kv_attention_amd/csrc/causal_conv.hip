@@ -31,6 +31,11 @@
 // Products use v_mfma_f32_16x16x32_bf16 with the weights as the A operand
 // (rows = output channels) and the pixels as the B columns, so a lane ends
 // with 4 consecutive output channels of one pixel: one 8-byte store each.
+//
+// Occupancy.  A one-frame chunk of a small grid has too few tiles for 256
+// CUs; then the K range is split by time offset (kt parts, one input frame
+// each), every part writes float32 partials, and a second kernel adds them
+// and the bias and rounds once.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -116,14 +121,15 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
   __shared__ __attribute__((aligned(1024))) char sw0[kTileBytes], sw1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sx0[kTileBytes], sx1[kTileBytes];
 
-  // Work unit (pixel tile, channel tile), channel tile fastest; each XCD
+  // Work unit (pixel tile, channel tile, split), split fastest; each XCD
   // gets a contiguous run of units so the tiles that share X share its L2.
   const int n_ct = p.c_out / kCout;
-  const int units = p.m_tiles * n_ct;
+  const int units = p.m_tiles * n_ct * p.splits;
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int per = units / kXcds, extra = units % kXcds;
   const int unit = xcd * per + (xcd < extra ? xcd : extra) + li;
-  const int mt = unit / n_ct, ct = unit % n_ct;
+  const int split = unit % p.splits;
+  const int mt = unit / p.splits / n_ct, ct = unit / p.splits % n_ct;
   const int m0 = mt * kPix, cout0 = ct * kCout;
   const int n_pix = p.frames * p.height * p.width;
 
@@ -156,9 +162,10 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
 #pragma unroll
   for (int s = 0; s < 2; ++s) rd[s] = c16 * kRowBytes + 16 * ((4 * s + h) ^ swz(c16));
 
-  const int taps = p.kt * p.kh * p.kw;
   const int n_cb = p.c_in / kCb;
-  const int n_blocks = taps * n_cb;
+  // this workgroup's K range: all taps, or the taps of time offset `split`
+  const int taps_per = p.kt * p.kh * p.kw / p.splits;
+  const int j_begin = split * taps_per * n_cb, j_end = j_begin + taps_per * n_cb;
   const long long w_tap_bytes = (long long)p.c_out * p.c_in * 2;
 
   const char* xsrc[kSlots];
@@ -213,21 +220,21 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
   };
 
-  set_tap(0);
-  fetch(0, sw0, sx0);
-  for (int j = 0; j < n_blocks; j += 2) {
+  set_tap(j_begin / n_cb);
+  fetch(j_begin, sw0, sx0);
+  for (int j = j_begin; j < j_end; j += 2) {
     // buffer 0 holds block j; block j+1 goes to buffer 1 meanwhile
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < n_blocks) {
+    if (j + 1 < j_end) {
       if ((j + 1) % n_cb == 0) set_tap((j + 1) / n_cb);
       fetch(j + 1, sw1, sx1);
     }
     compute(sw0, sx0);
-    if (j + 1 >= n_blocks) break;
+    if (j + 1 >= j_end) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 2 < n_blocks) {
+    if (j + 2 < j_end) {
       if ((j + 2) % n_cb == 0) set_tap((j + 2) / n_cb);
       fetch(j + 2, sw0, sx0);
     }
@@ -243,12 +250,38 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int co = cout0 + half_c * 64 + a * 16 + 4 * h;
+      if (p.splits > 1) {
+        *reinterpret_cast<float4*>(p.part + ((long long)split * n_pix + m) * p.c_out + co) =
+            make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+        continue;
+      }
       const float4 bias = *reinterpret_cast<const float4*>(p.bias + co);
       const bf16x2 lo = {(__bf16)(acc[a][b][0] + bias.x), (__bf16)(acc[a][b][1] + bias.y)};
       const bf16x2 hi = {(__bf16)(acc[a][b][2] + bias.z), (__bf16)(acc[a][b][3] + bias.w)};
       *reinterpret_cast<uint2*>(p.y + (long long)m * p.c_out + co) =
           make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     }
+  }
+}
+
+// Sum of the split partials plus bias, rounded to bf16 once (4 channels per
+// thread).
+__global__ __launch_bounds__(256) void conv_combine_kernel(ConvParams p) {
+  const long long n_pix = (long long)p.frames * p.height * p.width;
+  const long long total = n_pix * p.c_out / 4;
+  for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long long)gridDim.x * 256) {
+    const int co = (int)(u % (p.c_out / 4)) * 4;
+    float4 acc = *reinterpret_cast<const float4*>(p.bias + co);
+    for (int s = 0; s < p.splits; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(p.part + s * n_pix * p.c_out + u * 4);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const bf16x2 lo = {(__bf16)acc.x, (__bf16)acc.y};
+    const bf16x2 hi = {(__bf16)acc.z, (__bf16)acc.w};
+    reinterpret_cast<uint2*>(p.y)[u] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   }
 }
 
@@ -284,10 +317,18 @@ __global__ __launch_bounds__(256) void conv_pack_kernel(ConvPackParams p) {
 }  // namespace
 
 hipError_t launch_causal_conv(const ConvParams& p, hipStream_t s) {
-  const int units = p.m_tiles * (p.c_out / kCout);
+  const int units = p.m_tiles * (p.c_out / kCout) * p.splits;
   hipLaunchKernelGGL(causal_conv_kernel, dim3(units), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.splits > 1) {
+    const long long u4 = (long long)p.frames * p.height * p.width * p.c_out / 4;
+    long long blocks = (u4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(conv_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int first = p.frames > 2 ? p.frames - 2 : 0;
   const long long u4 = (long long)(p.frames - first) * p.height * p.width * p.c_in / 8;
   long long blocks = (u4 + 255) / 256;

@@ -3,8 +3,9 @@
 //
 // Host responsibilities: validate the config and every call, lay out the
 // caller's arena ([packed weights | float32 bias | 2-frame cache | zero
-// row]), keep the stream position (frames consumed since the last reset),
-// and launch the kernels on the caller's stream.  The cache needs no clearing
+// row | split partials]), keep the stream position (frames consumed since
+// the last reset), pick the split of the reduction over the time taps, and
+// launch the kernels on the caller's stream.  The cache needs no clearing
 // on reset: a frame before the video is never read from it (the kernel takes
 // the zero row instead).  Nothing here allocates device memory or
 // synchronises.
@@ -41,7 +42,7 @@ bool config_ok(const ckv_conv_config* c) {
 
 struct ConvLayout {
   size_t w_off = 0, w_bytes = 0;
-  size_t bias_off = 0, cache_off = 0, frame_bytes = 0, zero_off = 0, total = 0;
+  size_t bias_off = 0, cache_off = 0, frame_bytes = 0, zero_off = 0, part_off = 0, total = 0;
 };
 
 ConvLayout layout_of(const ckv_conv_config& c) {
@@ -53,8 +54,21 @@ ConvLayout layout_of(const ckv_conv_config& c) {
   L.cache_off = align_up(L.bias_off + sizeof(float) * c.out_channels);
   L.frame_bytes = (size_t)c.height * c.width * c.in_channels * sizeof(bf16_t);
   L.zero_off = align_up(L.cache_off + CKV_CONV_CACHE_T * L.frame_bytes);
-  L.total = align_up(L.zero_off + sizeof(bf16_t) * c.in_channels);
+  L.part_off = align_up(L.zero_off + sizeof(bf16_t) * c.in_channels);
+  // float32 partials of up to kt splits of the largest chunk (none for kt = 1)
+  const size_t part = c.kt > 1 ? sizeof(float) * c.kt * (size_t)c.max_frames * c.height * c.width * c.out_channels : 0;
+  L.total = align_up(L.part_off + part);
   return L;
+}
+
+// Split the reduction over the kt time offsets when one call's tiles would
+// leave CUs idle and the split parts still fit in two workgroups per CU
+// twice over; otherwise one pass over all taps.
+int splits_for(const ckv_conv_config& c, int frames, int num_cus) {
+  const long long pix = (long long)frames * c.height * c.width;
+  const long long units = (pix + ckv::kConvPixelTile - 1) / ckv::kConvPixelTile * (c.out_channels / ckv::kConvChannelTile);
+  const long long slots = 2LL * (num_cus > 0 ? num_cus : 256);
+  return c.kt > 1 && units * c.kt <= 2 * slots ? c.kt : 1;
 }
 
 bool ptr_ok(const void* p) { return p != nullptr && ((uintptr_t)p % 16) == 0; }
@@ -68,9 +82,22 @@ struct ckv_conv {
   bool dry;
   bool weights_set;
   long long position;  // frames consumed since the last reset
+  int num_cus;         // of the device the first call ran on (256 for a dry state)
   ckv_conv(const ckv_conv_config& c, char* a, bool d)
-      : cfg(c), L(layout_of(c)), arena(a), dry(d), weights_set(false), position(0) {}
+      : cfg(c), L(layout_of(c)), arena(a), dry(d), weights_set(false), position(0), num_cus(d ? 256 : 0) {}
 };
+
+namespace {
+ckv_status ensure_cus(ckv_conv* c) {
+  if (c->num_cus == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CKV_E_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return CKV_E_HIP;
+    c->num_cus = cus > 0 ? cus : 256;
+  }
+  return CKV_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -128,6 +155,7 @@ ckv_status ckv_causal_conv(ckv_conv* c, const void* x, int32_t frames, void* y, 
   if (x0 < y1 && y0 < x1) return CKV_E_INVALID;  // the kernel reads x while it writes y
   if (!c->weights_set) return CKV_E_STATE;
   if (!c->dry) {
+    if (ensure_cus(c) != CKV_OK) return CKV_E_HIP;
     ckv::ConvParams p{};
     p.x = static_cast<const bf16_t*>(x);
     p.y = static_cast<bf16_t*>(y);
@@ -145,6 +173,8 @@ ckv_status ckv_causal_conv(ckv_conv* c, const void* x, int32_t frames, void* y, 
     p.kh = c->cfg.kh;
     p.kw = c->cfg.kw;
     p.m_tiles = (int)((pix + ckv::kConvPixelTile - 1) / ckv::kConvPixelTile);
+    p.splits = splits_for(c->cfg, frames, c->num_cus);
+    p.part = reinterpret_cast<float*>(c->arena + c->L.part_off);
     if (ckv::launch_causal_conv(p, static_cast<hipStream_t>(stream)) != hipSuccess) return CKV_E_HIP;
   }
   c->position += frames;
@@ -152,6 +182,11 @@ ckv_status ckv_causal_conv(ckv_conv* c, const void* x, int32_t frames, void* y, 
 }
 
 int64_t ckv_conv_position(const ckv_conv* c) { return c ? c->position : -1; }
+
+int32_t ckv_conv_splits(const ckv_conv* c, int32_t frames) {
+  if (!c || frames < 1 || frames > c->cfg.max_frames) return 0;
+  return splits_for(c->cfg, frames, c->num_cus);
+}
 
 ckv_status ckv_conv_destroy(ckv_conv* c) {
   if (!c) return CKV_E_INVALID;

@@ -88,6 +88,8 @@ struct ConvParams {
   long long k0;              // global index of the chunk's first frame
   int frames, height, width, c_in, c_out, kt, kh, kw;
   int m_tiles;               // ceil(frames * H * W / kConvPixelTile)
+  int splits;                // 1, or kt: split s sums the taps of time offset s only
+  float* part;               // [splits][frames * H * W][C_out] float32 (splits > 1)
 };
 
 // Weights [C_out][C_in][taps] -> [taps][C_out][C_in], bias bf16 -> float32.

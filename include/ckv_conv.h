@@ -57,7 +57,8 @@ typedef struct ckv_conv_config {
 } ckv_conv_config;
 
 /* Arena bytes for one layer's state (packed weights, bias, the 2-frame
- * cache, a zero row); 0 if the config is invalid. */
+ * cache, a zero row, and float32 partials of a split call: kt * max_frames
+ * * H * W * C_out floats when kt > 1); 0 if the config is invalid. */
 size_t ckv_conv_bytes(const ckv_conv_config* cfg);
 
 /* Create a state object over a caller-owned device arena (>= ckv_conv_bytes,
@@ -90,6 +91,13 @@ ckv_status ckv_causal_conv(ckv_conv* c, const void* x, int32_t frames, void* y, 
 /* Frames consumed since the last reset (the global index of the next
  * chunk's first frame). */
 int64_t ckv_conv_position(const ckv_conv* c);
+
+/* How a call of `frames` frames splits its reduction: 1 (one pass over all
+ * taps) or kt (one part per time offset, float32 partials summed by a second
+ * kernel) -- chosen when the call's tiles alone would leave CUs idle.  The
+ * device's CU count is read on the first ckv_causal_conv; before that (and
+ * for a dry state) 256 is assumed.  0 for invalid arguments. */
+int32_t ckv_conv_splits(const ckv_conv* c, int32_t frames);
 
 ckv_status ckv_conv_destroy(ckv_conv* c);
 

@@ -18,11 +18,26 @@ def _cfg(**kw):
     return C.ConvConfig(**{**BASE.__dict__, **kw})
 
 
-def test_bytes_cover_weights_bias_cache_and_zero_row():
+def test_bytes_cover_weights_bias_cache_zero_row_and_partials():
     taps = 27
     need = taps * 384 * 384 * 2 + 384 * 4 + C.CONV_CACHE_T * 44 * 80 * 384 * 2 + 384 * 2
-    nbytes = C.conv_bytes(BASE)
-    assert need <= nbytes <= need + 4 * 256
+    partials = 3 * 4 * 44 * 80 * 384 * 4  # kt splits of a 4-frame chunk, float32
+    assert need + partials <= C.conv_bytes(BASE) <= need + partials + 5 * 256
+    one_tap = _cfg(kt=1)  # no split possible: no partials
+    need1 = 9 * 384 * 384 * 2 + 384 * 4 + C.CONV_CACHE_T * 44 * 80 * 384 * 2 + 384 * 2
+    assert need1 <= C.conv_bytes(one_tap) <= need1 + 5 * 256
+
+
+def test_split_policy():
+    """Split the reduction by time offset only when the call's tiles alone
+    would leave CUs idle (256 CUs, two workgroups each, assumed dry)."""
+    s = C.CausalConv(BASE, dry=True)
+    assert [s.splits(f) for f in (1, 2, 3, 4)] == [3, 3, 3, 3]   # 28..110 tiles x 3 channel tiles
+    assert s.splits(0) == 0 and s.splits(5) == 0
+    big = C.CausalConv(_cfg(height=88, width=160, max_frames=2), dry=True)
+    assert big.splits(1) == 3 and big.splits(2) == 1               # 330 -> 990 parts fit; 660 -> 1980 do not
+    assert C.CausalConv(_cfg(kt=1), dry=True).splits(1) == 1
+    assert C.CausalConv(_cfg(kt=2), dry=True).splits(1) == 2
 
 
 @pytest.mark.parametrize("bad", [dict(in_channels=32), dict(in_channels=96), dict(out_channels=64),

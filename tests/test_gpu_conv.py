@@ -63,12 +63,16 @@ def _check(got, ref, what, absum=None):
     return mx, rel
 
 
-def _case(cfg, chunks, seed=1, bias=True):
+def _case(cfg, chunks, seed=1, bias=True, splits=None):
+    """Stream the video in `chunks`; `splits` (if given) is the reduction split
+    every call must take."""
     G.require_gpu()
     print(f"[conv] {cfg} chunks={chunks} seed={seed} bias={bias}", flush=True)
     wb, bb = _layer(cfg, seed, bias)
     xb = _video(cfg, sum(chunks), seed)
     state = C.CausalConv(cfg)
+    if splits is not None:
+        assert all(state.splits(n) == splits for n in chunks)
     state.set_weights(G.to_dev(wb), None if bb is None else G.to_dev(bb))
     got = _stream(cfg, state, xb, chunks)
     x, w = I.bf16_bits_to_f64(xb), I.bf16_bits_to_f64(wb)
@@ -80,9 +84,17 @@ def _case(cfg, chunks, seed=1, bias=True):
 
 @pytest.mark.parametrize("chunks", [[1, 1, 1, 1], [1, 2, 1, 3], [4], [2, 2]])
 def test_tiny_ragged_grid_every_chunking(chunks):
-    """5 x 7 frames (35 pixels: tiles span rows and frames, ragged tail)."""
+    """5 x 7 frames (35 pixels: tiles span rows and frames, ragged tail);
+    small calls take the 3-way split of the reduction."""
     cfg = C.ConvConfig(height=5, width=7, in_channels=64, out_channels=128, max_frames=4)
-    _case(cfg, chunks)
+    _case(cfg, chunks, splits=3)
+
+
+def test_one_pass_path_with_three_time_taps():
+    """A grid large enough that calls take one pass over all 27 taps (no
+    split): 160 x 280 frames, 64 -> 128 channels, two one-frame chunks."""
+    cfg = C.ConvConfig(height=160, width=280, in_channels=64, out_channels=128, max_frames=1)
+    _case(cfg, [1, 1], seed=12, splits=1)
 
 
 @pytest.mark.parametrize("kernel", [(2, 3, 3), (1, 3, 3), (3, 1, 1), (1, 1, 1), (3, 1, 3), (3, 3, 1)])
@@ -94,7 +106,7 @@ def test_kernel_shapes(kernel):
 
 def test_several_channel_tiles_and_blocks_no_bias():
     cfg = C.ConvConfig(height=8, width=12, in_channels=192, out_channels=256, max_frames=2)
-    _case(cfg, [2, 1, 2, 1], seed=3, bias=False)
+    _case(cfg, [2, 1, 2, 1], seed=3, bias=False, splits=3)
 
 
 def test_reset_and_new_weights():
@@ -135,7 +147,7 @@ def test_decoder_layer_shape_full_compare():
     """The 384-channel 3x3x3 layer on the 44 x 80 latent grid of the 1280x704
     profile, 3 one-frame chunks then a 2-frame chunk, every output compared."""
     cfg = C.ConvConfig(height=44, width=80, in_channels=384, out_channels=384, max_frames=2)
-    mx, rel = _case(cfg, [1, 1, 1, 2], seed=7)
+    mx, rel = _case(cfg, [1, 1, 1, 2], seed=7, splits=3)
     print(f"[conv] 44x80x384: max {mx:.3e} rel {rel:.3e}", flush=True)
 
 
@@ -152,6 +164,7 @@ def test_bench_shape_sampled_pixels():
     state = C.CausalConv(cfg)
     state.set_weights(G.to_dev(wb), G.to_dev(bb))
     got = _stream(cfg, state, xb, [2, 2, 2])
+    assert state.splits(2) == 1
     x = I.bf16_bits_to_f64(xb)
     w = I.bf16_bits_to_f64(wb)
     b = I.bf16_bits_to_f64(bb)
