@@ -16,9 +16,11 @@ split, its small merge kernel), over all of its launches in the timed
 rollouts, timed with HIP events on the launch stream; the 880-query x
 19,360-key launches (chunks 19..28) are also reported on their own.  After
 the timed rollouts (outside them) it also reports the QK-Norm + RoPE + append
-path, a device copy of the append's byte count, and the cross-attention of an
-880-token chunk to a 512-row text context; `--no-extras` skips these, so that
-a profiled run traces only the rollout's launches.
+path, a device copy of the append's byte count, the cross-attention of an
+880-token chunk to a 512-row text context, and two streaming causal Conv3d
+layers of the VAE decoder (88x160 and 44x80 grids, 384 channels);
+`--no-extras` skips these, so that a profiled run traces only the rollout's
+launches.
 
 `--workload rollout30x2` times the whole model's attention traffic (30 layers
 x 2 prompts on 2 streams); `--workload attn880x19360` times the chunk-19
