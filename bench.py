@@ -182,11 +182,13 @@ def summarise_counters(fetch_csv, write_csv):
     print("\n".join(lines))
 
 
-def cpu_baseline(cfg, heads):
+def cpu_baseline(cfg, heads, calls=6):
     """The float64 oracle, untuned, on a bounded sample of the same workload:
-    the rotation of the window's keys (sink + chunks 1..18) and of chunk 19's
-    q/k, then chunk 19's attention (880 queries x 19,360 keys) for `heads`
-    heads.  Rate = that attention's algorithmic FLOPs / wall time."""
+    the rotation of the sink's and chunks 1..18's keys, then `calls` steady-
+    state chunk steps at step 0 (chunks 19, 20, ...: rotate q/k, record K/V,
+    attend 880 queries x 19,360 keys) for `heads` heads -- the rollout's
+    steady state, about 10 s of host work.  Rate = those attentions'
+    algorithmic FLOPs / wall time (rotations included in the time)."""
     import numpy as np
 
     import oracle.ckv_oracle as O
@@ -195,8 +197,9 @@ def cpu_baseline(cfg, heads):
     ocfg = O.OracleConfig(1, cfg.num_steps, heads, cfg.head_dim, cfg.grid_h, cfg.grid_w,
                           cfg.first_chunk_frames, cfg.window_chunks, cfg.max_chunks)
     ro = O.OracleRollout(ocfg)
+    last = 18 + calls
     data = {}
-    for c in range(0, 20):
+    for c in range(0, last + 1):
         n = cfg.tokens(c)
         data[c] = [I.bf16_bits_to_f64(b) for b in
                    I.draw_qkv_bits(n, heads, cfg.head_dim, base_seed=0, chunk=c, step_code=4 if c == 0 else 0)]
@@ -209,10 +212,11 @@ def cpu_baseline(cfg, heads):
     ro.sink[0] = (ro.rotate(0, data[0][1]), data[0][2])
     for c in range(1, 19):
         ro.noisy[(0, 0, c)] = (ro.rotate(c, data[c][1]), data[c][2])
-    out, _ = ro.chunk_step(0, 0, 19, *data[19])
+    for c in range(19, last + 1):
+        out, _ = ro.chunk_step(0, 0, c, *data[c])
+        assert np.isfinite(out).all()
     dt = time.perf_counter() - t0
-    assert np.isfinite(out).all()
-    flops = 4 * cfg.tokens(19) * keys_of(cfg, 19) * heads * cfg.head_dim
+    flops = sum(4 * cfg.tokens(c) * keys_of(cfg, c) * heads * cfg.head_dim for c in range(19, last + 1))
     cpu_model = platform.processor() or ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -223,8 +227,8 @@ def cpu_baseline(cfg, heads):
         pass
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": (f"float64 numpy oracle: RoPE of the window's keys (sink + chunks 1..18) and chunk 19's "
-                   f"q/k, then chunk 19's attention 880 x 19,360 keys for {heads} of 24 heads; "
+        "sample": (f"float64 numpy oracle: RoPE of the sink's and chunks 1..18's keys, then chunks "
+                   f"19..{last} at step 0 (RoPE, record, attention 880 x 19,360 keys) for {heads} of 24 heads; "
                    f"{flops / 1e9:.1f} GFLOP in {dt:.2f} s"),
         "seconds": dt, "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
     }
