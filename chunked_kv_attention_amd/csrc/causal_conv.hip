@@ -264,9 +264,29 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
   }
 }
 
-// Sum of the split partials plus bias, rounded to bf16 once (4 channels per
-// thread).
-__global__ __launch_bounds__(256) void conv_combine_kernel(ConvParams p) {
+// Keep the last two input frames of the stream: frame f of the chunk is
+// global frame k0 + f and goes to cache slot (k0 + f) mod 2 (frames
+// first_frame .. frames-1; grid-stride over 16-byte units).
+__device__ inline void copy_to_cache(const ConvParams& p, int first_frame) {
+  const long long frame_u4 = (long long)p.height * p.width * p.c_in / 8;  // 16-byte units per frame
+  const long long total = (p.frames - first_frame) * frame_u4;
+  for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long long)gridDim.x * 256) {
+    const int f = first_frame + (int)(u / frame_u4);
+    const long long e = u % frame_u4;
+    const uint4* src = reinterpret_cast<const uint4*>(p.x) + f * frame_u4 + e;
+    uint4* dst = reinterpret_cast<uint4*>(p.cache) + ((p.k0 + f) & 1) * frame_u4 + e;
+    *dst = *src;
+  }
+}
+
+__global__ __launch_bounds__(256) void conv_cache_kernel(ConvParams p, int first_frame) {
+  copy_to_cache(p, first_frame);
+}
+
+// After a split call: the sum of the partials plus bias, rounded to bf16 once
+// (4 channels per thread), then the cache update (every conv workgroup has
+// finished reading the cache by now).
+__global__ __launch_bounds__(256) void conv_combine_kernel(ConvParams p, int first_frame) {
   const long long n_pix = (long long)p.frames * p.height * p.width;
   const long long total = n_pix * p.c_out / 4;
   for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long long)gridDim.x * 256) {
@@ -283,20 +303,7 @@ __global__ __launch_bounds__(256) void conv_combine_kernel(ConvParams p) {
     const bf16x2 hi = {(__bf16)acc.z, (__bf16)acc.w};
     reinterpret_cast<uint2*>(p.y)[u] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   }
-}
-
-// Keep the last two input frames of the stream: frame f of the chunk is
-// global frame k0 + f and goes to cache slot (k0 + f) mod 2.
-__global__ __launch_bounds__(256) void conv_cache_kernel(ConvParams p, int first_frame) {
-  const long long frame_u4 = (long long)p.height * p.width * p.c_in / 8;  // 16-byte units per frame
-  const long long total = (p.frames - first_frame) * frame_u4;
-  for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long long)gridDim.x * 256) {
-    const int f = first_frame + (int)(u / frame_u4);
-    const long long e = u % frame_u4;
-    const uint4* src = reinterpret_cast<const uint4*>(p.x) + f * frame_u4 + e;
-    uint4* dst = reinterpret_cast<uint4*>(p.cache) + ((p.k0 + f) & 1) * frame_u4 + e;
-    *dst = *src;
-  }
+  copy_to_cache(p, first_frame);
 }
 
 // Weights [C_out][C_in][taps] -> [taps][C_out][C_in]; bias bf16 -> float32
@@ -321,19 +328,18 @@ hipError_t launch_causal_conv(const ConvParams& p, hipStream_t s) {
   hipLaunchKernelGGL(causal_conv_kernel, dim3(units), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.splits > 1) {
-    const long long u4 = (long long)p.frames * p.height * p.width * p.c_out / 4;
-    long long blocks = (u4 + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(conv_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const int first = p.frames > 2 ? p.frames - 2 : 0;
-  const long long u4 = (long long)(p.frames - first) * p.height * p.width * p.c_in / 8;
-  long long blocks = (u4 + 255) / 256;
+  long long work = (long long)(p.frames - first) * p.height * p.width * p.c_in / 8;  // cache units
+  if (p.splits > 1) {
+    const long long out4 = (long long)p.frames * p.height * p.width * p.c_out / 4;
+    if (out4 > work) work = out4;
+  }
+  long long blocks = (work + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(conv_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, first);
+  if (p.splits > 1)
+    hipLaunchKernelGGL(conv_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, first);
+  else
+    hipLaunchKernelGGL(conv_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, first);
   return hipGetLastError();
 }
 
