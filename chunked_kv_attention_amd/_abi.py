@@ -106,7 +106,7 @@ def load() -> ctypes.CDLL:
         "ckv_conv_reset": (I32, [P]),
         "ckv_causal_conv": (I32, [P, P, I32, P, P]),
         "ckv_conv_position": (ctypes.c_int64, [P]),
-        "ckv_conv_splits": (I32, [P, I32]),
+        "ckv_conv_splits": (I32, [P, I32, ctypes.POINTER(I32)]),
         "ckv_conv_destroy": (I32, [P]),
     }
     for name, (res, args) in sig.items():
@@ -399,7 +399,14 @@ class CausalConv:
         return int(self._lib.ckv_conv_position(self._h))
 
     def splits(self, frames: int) -> int:
-        return int(self._lib.ckv_conv_splits(self._h, int(frames)))
+        """Parts of each split unit of a call (1: none split)."""
+        return self.plan(frames)[1]
+
+    def plan(self, frames: int):
+        """(units run whole, parts of every later unit) for a call of `frames`."""
+        whole = ctypes.c_int32()
+        parts = int(self._lib.ckv_conv_splits(self._h, int(frames), ctypes.byref(whole)))
+        return whole.value, parts
 
     def reset(self):
         _check(self._lib.ckv_conv_reset(self._h), "ckv_conv_reset")

@@ -33,9 +33,10 @@
 // with 4 consecutive output channels of one pixel: one 8-byte store each.
 //
 // Occupancy.  A one-frame chunk of a small grid has too few tiles for 256
-// CUs; then the K range is split by time offset (kt parts, one input frame
-// each), every part writes float32 partials, and a second kernel adds them
-// and the bias and rounds once.
+// CUs, and a larger call may leave a last, partly filled round of tiles;
+// such tiles are split by time offset (kt parts, one input frame each),
+// every part writes float32 partials, and a second kernel adds them and the
+// bias and rounds once.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -121,15 +122,23 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
   __shared__ __attribute__((aligned(1024))) char sw0[kTileBytes], sw1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sx0[kTileBytes], sx1[kTileBytes];
 
-  // Work unit (pixel tile, channel tile, split), split fastest; each XCD
-  // gets a contiguous run of units so the tiles that share X share its L2.
+  // Work item -> (unit, part).  Blocks [0, whole) run whole units, the rest
+  // run the parts of the later units, part fastest.  Within each of the two
+  // ranges every XCD gets a contiguous run of items, so the tiles that share
+  // X share its L2 (blocks go round-robin over the 8 XCDs).
   const int n_ct = p.c_out / kCout;
-  const int units = p.m_tiles * n_ct * p.splits;
-  const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
-  const int per = units / kXcds, extra = units % kXcds;
-  const int unit = xcd * per + (xcd < extra ? xcd : extra) + li;
-  const int split = unit % p.splits;
-  const int mt = unit / p.splits / n_ct, ct = unit / p.splits % n_ct;
+  const int units = p.m_tiles * n_ct;
+  const bool in_whole = (int)blockIdx.x < p.whole;
+  const int r0 = in_whole ? 0 : p.whole;
+  const int rlen = in_whole ? p.whole : (units - p.whole) * p.splits;
+  const int b = blockIdx.x - r0;
+  const int xcd = b % kXcds, li = b / kXcds;
+  const int per = rlen / kXcds, extra = rlen % kXcds;
+  const int item = xcd * per + (xcd < extra ? xcd : extra) + li;
+  const int parts = in_whole ? 1 : p.splits;
+  const int split = in_whole ? 0 : item % p.splits;
+  const int unit = in_whole ? item : p.whole + item / p.splits;
+  const int mt = unit / n_ct, ct = unit % n_ct;
   const int m0 = mt * kPix, cout0 = ct * kCout;
   const int n_pix = p.frames * p.height * p.width;
 
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
 
   const int n_cb = p.c_in / kCb;
   // this workgroup's K range: all taps, or the taps of time offset `split`
-  const int taps_per = p.kt * p.kh * p.kw / p.splits;
+  const int taps_per = p.kt * p.kh * p.kw / parts;
   const int j_begin = split * taps_per * n_cb, j_end = j_begin + taps_per * n_cb;
   const long long w_tap_bytes = (long long)p.c_out * p.c_in * 2;
 
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void causal_conv_kernel(ConvParams p) 
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int co = cout0 + half_c * 64 + a * 16 + 4 * h;
-      if (p.splits > 1) {
+      if (parts > 1) {
         *reinterpret_cast<float4*>(p.part + ((long long)split * n_pix + m) * p.c_out + co) =
             make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
         continue;
@@ -283,17 +292,23 @@ __global__ __launch_bounds__(256) void conv_cache_kernel(ConvParams p, int first
   copy_to_cache(p, first_frame);
 }
 
-// After a split call: the sum of the partials plus bias, rounded to bf16 once
-// (4 channels per thread), then the cache update (every conv workgroup has
-// finished reading the cache by now).
+// After a call with split units: for each of their outputs, the sum of the
+// partials plus bias, rounded to bf16 once (4 channels per thread), then the
+// cache update (every conv workgroup has finished reading the cache by now).
 __global__ __launch_bounds__(256) void conv_combine_kernel(ConvParams p, int first_frame) {
   const long long n_pix = (long long)p.frames * p.height * p.width;
-  const long long total = n_pix * p.c_out / 4;
+  const int n_ct = p.c_out / kCout;
+  const long long per_unit = (long long)kPix * kCout / 4;
+  const long long total = (long long)(p.m_tiles * n_ct - p.whole) * per_unit;
   for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < total; u += (long long)gridDim.x * 256) {
-    const int co = (int)(u % (p.c_out / 4)) * 4;
+    const int unit = p.whole + (int)(u / per_unit);
+    const int r = (int)(u % per_unit);
+    const long long m = (long long)(unit / n_ct) * kPix + r / (kCout / 4);
+    const int co = (unit % n_ct) * kCout + (r % (kCout / 4)) * 4;
+    if (m >= n_pix) continue;
     float4 acc = *reinterpret_cast<const float4*>(p.bias + co);
     for (int s = 0; s < p.splits; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(p.part + s * n_pix * p.c_out + u * 4);
+      const float4 v = *reinterpret_cast<const float4*>(p.part + (s * n_pix + m) * p.c_out + co);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -301,7 +316,8 @@ __global__ __launch_bounds__(256) void conv_combine_kernel(ConvParams p, int fir
     }
     const bf16x2 lo = {(__bf16)acc.x, (__bf16)acc.y};
     const bf16x2 hi = {(__bf16)acc.z, (__bf16)acc.w};
-    reinterpret_cast<uint2*>(p.y)[u] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    *reinterpret_cast<uint2*>(p.y + m * p.c_out + co) =
+        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   }
   copy_to_cache(p, first_frame);
 }
@@ -324,19 +340,21 @@ __global__ __launch_bounds__(256) void conv_pack_kernel(ConvPackParams p) {
 }  // namespace
 
 hipError_t launch_causal_conv(const ConvParams& p, hipStream_t s) {
-  const int units = p.m_tiles * (p.c_out / kCout) * p.splits;
-  hipLaunchKernelGGL(causal_conv_kernel, dim3(units), dim3(kThreads), 0, s, p);
+  const int units = p.m_tiles * (p.c_out / kCout);
+  const int split_units = units - p.whole;
+  const int blocks_conv = p.whole + split_units * p.splits;
+  hipLaunchKernelGGL(causal_conv_kernel, dim3(blocks_conv), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int first = p.frames > 2 ? p.frames - 2 : 0;
   long long work = (long long)(p.frames - first) * p.height * p.width * p.c_in / 8;  // cache units
-  if (p.splits > 1) {
-    const long long out4 = (long long)p.frames * p.height * p.width * p.c_out / 4;
+  if (split_units > 0) {
+    const long long out4 = (long long)split_units * kPix * kCout / 4;
     if (out4 > work) work = out4;
   }
   long long blocks = (work + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  if (p.splits > 1)
+  if (split_units > 0)
     hipLaunchKernelGGL(conv_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, first);
   else
     hipLaunchKernelGGL(conv_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, first);

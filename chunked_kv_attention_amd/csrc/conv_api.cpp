@@ -4,7 +4,7 @@
 // Host responsibilities: validate the config and every call, lay out the
 // caller's arena ([packed weights | float32 bias | 2-frame cache | zero
 // row | split partials]), keep the stream position (frames consumed since
-// the last reset), pick the split of the reduction over the time taps, and
+// the last reset), plan which tiles split their reduction by time offset, and
 // launch the kernels on the caller's stream.  The cache needs no clearing
 // on reset: a frame before the video is never read from it (the kernel takes
 // the zero row instead).  Nothing here allocates device memory or
@@ -61,14 +61,25 @@ ConvLayout layout_of(const ckv_conv_config& c) {
   return L;
 }
 
-// Split the reduction over the kt time offsets when one call's tiles would
-// leave CUs idle and the split parts still fit in two workgroups per CU
-// twice over; otherwise one pass over all taps.
-int splits_for(const ckv_conv_config& c, int frames, int num_cus) {
+// How a call's units (pixel tile, channel tile) run, with two workgroups per
+// CU as the slots: all of them split kt ways by time offset when even the
+// split parts fill at most two rounds of slots; otherwise whole, except a
+// last, partly filled round, whose units are split when their parts fit in
+// one round; whole throughout for kt = 1.
+struct SplitPlan {
+  int whole;   // units run over all taps
+  int splits;  // parts of every later unit
+};
+
+SplitPlan plan_for(const ckv_conv_config& c, int frames, int num_cus) {
   const long long pix = (long long)frames * c.height * c.width;
   const long long units = (pix + ckv::kConvPixelTile - 1) / ckv::kConvPixelTile * (c.out_channels / ckv::kConvChannelTile);
   const long long slots = 2LL * (num_cus > 0 ? num_cus : 256);
-  return c.kt > 1 && units * c.kt <= 2 * slots ? c.kt : 1;
+  if (c.kt == 1) return SplitPlan{(int)units, 1};
+  if (units * c.kt <= 2 * slots) return SplitPlan{0, c.kt};
+  const long long tail = units % slots;
+  if (tail > 0 && tail * c.kt <= slots) return SplitPlan{(int)(units - tail), c.kt};
+  return SplitPlan{(int)units, 1};
 }
 
 bool ptr_ok(const void* p) { return p != nullptr && ((uintptr_t)p % 16) == 0; }
@@ -173,7 +184,9 @@ ckv_status ckv_causal_conv(ckv_conv* c, const void* x, int32_t frames, void* y, 
     p.kh = c->cfg.kh;
     p.kw = c->cfg.kw;
     p.m_tiles = (int)((pix + ckv::kConvPixelTile - 1) / ckv::kConvPixelTile);
-    p.splits = splits_for(c->cfg, frames, c->num_cus);
+    const SplitPlan plan = plan_for(c->cfg, frames, c->num_cus);
+    p.whole = plan.whole;
+    p.splits = plan.splits;
     p.part = reinterpret_cast<float*>(c->arena + c->L.part_off);
     if (ckv::launch_causal_conv(p, static_cast<hipStream_t>(stream)) != hipSuccess) return CKV_E_HIP;
   }
@@ -183,9 +196,11 @@ ckv_status ckv_causal_conv(ckv_conv* c, const void* x, int32_t frames, void* y, 
 
 int64_t ckv_conv_position(const ckv_conv* c) { return c ? c->position : -1; }
 
-int32_t ckv_conv_splits(const ckv_conv* c, int32_t frames) {
+int32_t ckv_conv_splits(const ckv_conv* c, int32_t frames, int32_t* whole_units) {
   if (!c || frames < 1 || frames > c->cfg.max_frames) return 0;
-  return splits_for(c->cfg, frames, c->num_cus);
+  const SplitPlan plan = plan_for(c->cfg, frames, c->num_cus);
+  if (whole_units) *whole_units = plan.whole;
+  return plan.splits;
 }
 
 ckv_status ckv_conv_destroy(ckv_conv* c) {

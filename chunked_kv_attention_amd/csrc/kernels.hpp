@@ -88,8 +88,12 @@ struct ConvParams {
   long long k0;              // global index of the chunk's first frame
   int frames, height, width, c_in, c_out, kt, kh, kw;
   int m_tiles;               // ceil(frames * H * W / kConvPixelTile)
-  int splits;                // 1, or kt: split s sums the taps of time offset s only
-  float* part;               // [splits][frames * H * W][C_out] float32 (splits > 1)
+  // Units (pixel tile, channel tile) 0 .. whole-1 run over all taps; each
+  // later unit runs as `splits` parts, part s summing the taps of time offset
+  // s only and writing float32 partials (splits = 1: no split units).
+  int whole;
+  int splits;                // 1, or kt
+  float* part;               // [splits][frames * H * W][C_out] float32 (split units)
 };
 
 // Weights [C_out][C_in][taps] -> [taps][C_out][C_in], bias bf16 -> float32.

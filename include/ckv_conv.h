@@ -92,12 +92,15 @@ ckv_status ckv_causal_conv(ckv_conv* c, const void* x, int32_t frames, void* y, 
  * chunk's first frame). */
 int64_t ckv_conv_position(const ckv_conv* c);
 
-/* How a call of `frames` frames splits its reduction: 1 (one pass over all
- * taps) or kt (one part per time offset, float32 partials summed by a second
- * kernel) -- chosen when the call's tiles alone would leave CUs idle.  The
- * device's CU count is read on the first ckv_causal_conv; before that (and
- * for a dry state) 256 is assumed.  0 for invalid arguments. */
-int32_t ckv_conv_splits(const ckv_conv* c, int32_t frames);
+/* How a call of `frames` frames runs its (pixel tile, channel tile) units:
+ * the first *whole_units of them (if whole_units is not NULL) over all taps,
+ * every later one as `return value` parts, part s summing the taps of time
+ * offset s (float32 partials, summed with the bias by a second kernel).
+ * Units split when the call alone would leave CUs idle, or when they form a
+ * last, partly filled round of two workgroups per CU.  The device's CU count
+ * is read on the first ckv_causal_conv; before that (and for a dry state)
+ * 256 is assumed.  Returns 0 for invalid arguments. */
+int32_t ckv_conv_splits(const ckv_conv* c, int32_t frames, int32_t* whole_units);
 
 ckv_status ckv_conv_destroy(ckv_conv* c);
 

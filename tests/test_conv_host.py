@@ -29,15 +29,21 @@ def test_bytes_cover_weights_bias_cache_zero_row_and_partials():
 
 
 def test_split_policy():
-    """Split the reduction by time offset only when the call's tiles alone
-    would leave CUs idle (256 CUs, two workgroups each, assumed dry)."""
+    """Which units split their reduction by time offset (256 CUs assumed dry,
+    two workgroups each = 512 slots): every unit when even the split parts
+    fill at most two rounds; otherwise only a last, partly filled round whose
+    parts fit in one round; never for kt = 1."""
     s = C.CausalConv(BASE, dry=True)
-    assert [s.splits(f) for f in (1, 2, 3, 4)] == [3, 3, 3, 3]   # 28..110 tiles x 3 channel tiles
+    assert [s.plan(f) for f in (1, 2, 3, 4)] == [(0, 3)] * 4        # 84..330 units of 44x80 frames
     assert s.splits(0) == 0 and s.splits(5) == 0
-    big = C.CausalConv(_cfg(height=88, width=160, max_frames=2), dry=True)
-    assert big.splits(1) == 3 and big.splits(2) == 1               # 330 -> 990 parts fit; 660 -> 1980 do not
-    assert C.CausalConv(_cfg(kt=1), dry=True).splits(1) == 1
-    assert C.CausalConv(_cfg(kt=2), dry=True).splits(1) == 2
+    big = C.CausalConv(_cfg(height=88, width=160, max_frames=3), dry=True)
+    assert big.plan(1) == (0, 3)                                     # 330 units -> 990 parts
+    assert big.plan(2) == (512, 3)                                   # 660 units: last 148 split -> 444 parts
+    assert big.plan(3) == (990, 1)                                   # 990 units: last 478 would need 1434 parts
+    assert C.CausalConv(_cfg(kt=1), dry=True).plan(1) == (84, 1)
+    assert C.CausalConv(_cfg(kt=2), dry=True).plan(1) == (0, 2)
+    exact = C.CausalConv(_cfg(height=64, width=256, out_channels=128, max_frames=8), dry=True)
+    assert exact.plan(8) == (1024, 1)                                # 1024 units: two full rounds, no tail
 
 
 @pytest.mark.parametrize("bad", [dict(in_channels=32), dict(in_channels=96), dict(out_channels=64),

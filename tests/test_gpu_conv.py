@@ -63,9 +63,10 @@ def _check(got, ref, what, absum=None):
     return mx, rel
 
 
-def _case(cfg, chunks, seed=1, bias=True, splits=None):
-    """Stream the video in `chunks`; `splits` (if given) is the reduction split
-    every call must take."""
+def _case(cfg, chunks, seed=1, bias=True, splits=None, hybrid=False):
+    """Stream the video in `chunks`; `splits` (if given) is the parts of the
+    split units every call must take; `hybrid` asks that some units run whole
+    and the rest split."""
     G.require_gpu()
     print(f"[conv] {cfg} chunks={chunks} seed={seed} bias={bias}", flush=True)
     wb, bb = _layer(cfg, seed, bias)
@@ -75,6 +76,10 @@ def _case(cfg, chunks, seed=1, bias=True, splits=None):
         assert all(state.splits(n) == splits for n in chunks)
     state.set_weights(G.to_dev(wb), None if bb is None else G.to_dev(bb))
     got = _stream(cfg, state, xb, chunks)
+    if hybrid:  # the device's CU count is known after the first call
+        units = -(-chunks[-1] * cfg.height * cfg.width // 128) * (cfg.out_channels // 128)
+        whole, parts = state.plan(chunks[-1])
+        assert 0 < whole < units and parts == cfg.kt, (whole, parts, units)
     x, w = I.bf16_bits_to_f64(xb), I.bf16_bits_to_f64(wb)
     ref = CO.causal_conv3d(x, w, None if bb is None else I.bf16_bits_to_f64(bb))
     absum = CO.causal_conv3d(np.abs(x), np.abs(w)) + (0.0 if bb is None else np.abs(I.bf16_bits_to_f64(bb)))
@@ -102,6 +107,14 @@ def test_kernel_shapes(kernel):
     kt, kh, kw = kernel
     cfg = C.ConvConfig(height=6, width=9, in_channels=64, out_channels=128, kt=kt, kh=kh, kw=kw, max_frames=3)
     _case(cfg, [1, 3, 1, 2], seed=2)
+
+
+def test_last_round_split_path():
+    """A call with more units than one round of workgroup slots: the first
+    full round runs whole, the units of the partly filled last round run as 3
+    parts (240 x 320 frames: 600 units on 256 CUs -> 512 whole + 88 x 3)."""
+    cfg = C.ConvConfig(height=240, width=320, in_channels=64, out_channels=128, max_frames=1)
+    _case(cfg, [1, 1], seed=13, hybrid=True)
 
 
 def test_several_channel_tiles_and_blocks_no_bias():
@@ -153,9 +166,9 @@ def test_decoder_layer_shape_full_compare():
 
 def test_bench_shape_sampled_pixels():
     """The benchmarked layer (88 x 160 grid, 384 -> 384, 2-frame chunks) at
-    full size: three chunks streamed, then 64 sampled output pixels of the
-    last chunk (all channels) computed one by one by the oracle from the
-    frames that reach them."""
+    full size: three chunks streamed, then 84 sampled output pixels of the
+    last chunk (all channels; 20 of them in the units that split) computed
+    one by one by the oracle from the frames that reach them."""
     G.require_gpu()
     cfg = C.ConvConfig(height=88, width=160, in_channels=384, out_channels=384, max_frames=2)
     print(f"[conv] {cfg} sampled", flush=True)
@@ -164,13 +177,16 @@ def test_bench_shape_sampled_pixels():
     state = C.CausalConv(cfg)
     state.set_weights(G.to_dev(wb), G.to_dev(bb))
     got = _stream(cfg, state, xb, [2, 2, 2])
-    assert state.splits(2) == 1
+    whole, parts = state.plan(2)
+    assert 0 < whole < 660 and parts == 3  # the last round's units split (660 units, 512 slots)
     x = I.bf16_bits_to_f64(xb)
     w = I.bf16_bits_to_f64(wb)
     b = I.bf16_bits_to_f64(bb)
     rng = np.random.default_rng(9)
     picks = [(t, int(rng.integers(cfg.height)), int(rng.integers(cfg.width))) for t in (4, 5) for _ in range(30)]
     picks += [(4, 0, 0), (5, cfg.height - 1, cfg.width - 1), (4, 0, cfg.width - 1), (5, cfg.height - 1, 0)]
+    # pixels of the split units (unit >= 512 of the chunk: its second frame, rows >= 48)
+    picks += [(5, int(rng.integers(48, cfg.height)), int(rng.integers(cfg.width))) for _ in range(20)]
     ref, out, absum = [], [], []
     for t, i, j in picks:
         # the oracle on the 3 x 3 x 3 neighbourhood that reaches (t, i, j)
