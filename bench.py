@@ -519,7 +519,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the same-step chunk attention path is built and timed on a single "
-              "MI355X (head-sharding across GPUs is a design note, not part of this build). Run with --gpus 1.",
+              "MI355X; sharding heads across GPUs is described in the design notes, not implemented. Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: device transfer of bf16 bit patterns, the
-comparison metrics, and a driver that runs the same seeded rollout through the
+comparison metrics, and a helper that runs the same seeded rollout through the
 C-ABI and through the oracle."""
 
 from __future__ import annotations
