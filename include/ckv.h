@@ -90,8 +90,9 @@ typedef struct ckv_segment {
   int32_t n_tokens;    /* keys in the run                                                   */
 } ckv_segment;
 
-/* Device bytes a cache with this config needs (sinks + rings + angle tables +
- * split-key scratch), or 0 if the config is invalid. */
+/* Device bytes a cache with this config needs (angle tables + sinks + rings +
+ * one text context per layer + split-key scratch), or 0 if the config is
+ * invalid. */
 size_t ckv_cache_bytes(const ckv_config* cfg);
 
 /* Create a cache over a caller-owned device arena of at least
@@ -99,7 +100,8 @@ size_t ckv_cache_bytes(const ckv_config* cfg);
  * memory (the angle tables are uploaded by the first rope_append/sink_build,
  * on that call's stream).  Sink and ring layout inside the arena:
  *   sink  K [L][H][F0*gh*gw][d],  V transposed [L][H][d][F0*gh*gw];
- *   rings K [L][S][H][(W+1)*gh*gw][d], V transposed [L][S][H][d][(W+1)*gh*gw].
+ *   rings K [L][S][H][(W+1)*gh*gw][d], V transposed [L][S][H][d][(W+1)*gh*gw];
+ *   text  K [L][H][CKV_MAX_TEXT_TOKENS][d], V transposed [L][H][d][CKV_MAX_TEXT_TOKENS].
  * Errors: CKV_E_INVALID (config), CKV_E_ARENA (arena). */
 ckv_status ckv_cache_create(const ckv_config* cfg, void* device_arena, size_t arena_bytes,
                             ckv_cache** out);
