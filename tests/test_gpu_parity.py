@@ -6,6 +6,8 @@ relative L2 <= 5e-3 against the oracle on the same bf16 inputs.  Small shapes
 are compared on every element; full-size shapes on sampled rows (all heads,
 all head dims) that include the first and last rows and tile edges."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -194,6 +196,17 @@ def test_tiny_rollout_every_chunk_and_step():
     r.run_first_chunk()
     r.run_chunks(range(1, 6))
     print(f"tiny rollout worst: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
+
+
+def test_config_rope_base_and_softmax_scale():
+    """A rollout with a non-default RoPE base (500) and an explicit softmax
+    scale (0.2 instead of 1/sqrt(64)) through both config fields; every
+    output element of every call against the oracle given the same values."""
+    cfg = dataclasses.replace(TINY, rope_theta=500.0, softmax_scale=0.2)
+    r = G.Rollout(cfg, base_seed=17)
+    r.run_first_chunk()
+    r.run_chunks(range(1, 6))
+    print(f"theta 500, scale 0.2: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
 
 
 def test_window_membership_on_device():
