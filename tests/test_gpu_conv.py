@@ -156,6 +156,40 @@ def test_streaming_equals_one_call_bitwise():
         np.testing.assert_array_equal(o, outs[0])
 
 
+def test_two_layers_on_two_streams():
+    """Two independent states (two layers, or two videos) streamed on two HIP
+    streams at once, chunks interleaved; each matches its own whole-video
+    oracle."""
+    G.require_gpu()
+    cfg = C.ConvConfig(height=12, width=20, in_channels=128, out_channels=128, max_frames=2)
+    chunks = [1, 2, 1, 2]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cases = []
+    for k in range(2):
+        wb, bb = _layer(cfg, 20 + k)
+        xb = _video(cfg, sum(chunks), 30 + k)
+        state = C.CausalConv(cfg)
+        w_dev, b_dev = G.to_dev(wb), G.to_dev(bb)
+        torch.cuda.synchronize()  # uploads done before the other stream packs them
+        state.set_weights(w_dev, b_dev, stream=streams[k])
+        cases.append((state, wb, bb, xb, [w_dev, b_dev]))
+    t0 = 0
+    for n in chunks:
+        for k, (state, _, _, xb, outs) in enumerate(cases):
+            with torch.cuda.stream(streams[k]):
+                x = G.to_dev(xb[t0:t0 + n])
+                y = torch.empty((n, cfg.height, cfg.width, cfg.out_channels), dtype=torch.bfloat16, device="cuda")
+                state(x, y, stream=streams[k])
+                outs.append((x, y))
+        t0 += n
+    torch.cuda.synchronize()
+    for state, wb, bb, xb, outs in cases:
+        got = np.concatenate([G.from_dev(y) for _, y in outs[2:]])
+        x, w, b = I.bf16_bits_to_f64(xb), I.bf16_bits_to_f64(wb), I.bf16_bits_to_f64(bb)
+        ref = CO.causal_conv3d(x, w, b)
+        _check(got, ref, "two streams", CO.causal_conv3d(np.abs(x), np.abs(w)) + np.abs(b))
+
+
 def test_decoder_layer_shape_full_compare():
     """The 384-channel 3x3x3 layer on the 44 x 80 latent grid of the 1280x704
     profile, 3 one-frame chunks then a 2-frame chunk, every output compared."""
