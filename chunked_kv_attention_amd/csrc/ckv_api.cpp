@@ -183,7 +183,10 @@ int splits_for(int num_cus, int heads, int n_queries, int n_keys) {
   const long long slots = 2LL * (num_cus > 0 ? num_cus : 256);  // two workgroups per CU
   long long p = slots / (units > 0 ? units : 1);
   if (p > kMaxSplits) p = kMaxSplits;
-  if (p > key_tiles / 4) p = key_tiles / 4;  // keep >= 4 key tiles per split
+  // keep >= 8 key tiles per split: below that the merge kernel and the
+  // partials cost more than the idle CUs of an unsplit call (measured: an
+  // 880 x 512 cross-attention takes 16 us unsplit, 26 us split in two)
+  if (p > key_tiles / 8) p = key_tiles / 8;
   return p < 1 ? 1 : (int)p;
 }
 

@@ -199,8 +199,12 @@ def test_attention_splits_policy():
     assert cache.attention_splits(880, 19360) == 3
     # 2640 x 24 = 504 workgroups already fill the chip
     assert cache.attention_splits(2640, 2640) == 1
-    # never fewer than 4 key tiles per split
-    assert cache.attention_splits(880, 64 * 7) == 1
+    # never fewer than 8 key tiles per split: a 512-row text context runs unsplit
+    assert cache.attention_splits(880, 64 * 15) == 1
+    assert cache.attention_splits(880, 512) == 1
+    assert cache.attention_splits(880, 64 * 16) == 2
+    # every chunk window of the rollout (>= 3,520 keys) keeps the 3-way split
+    assert cache.attention_splits(880, 3520) == 3
 
 
 def test_norm_entry_points_validate_and_follow_the_schedule():

@@ -298,12 +298,14 @@ def test_ragged_query_and_key_tiles_two_layers():
 
 
 def test_split_keys_path_head_dim_64():
-    """A shape where the key range is split (and merged) with head_dim 64."""
-    cfg = C.Config(1, 1, 2, 64, 8, 8, 3, 6, 9)
+    """A shape where the key range is split (and merged) with head_dim 64:
+    8 x 8 frames, window 14 chunks, so the later windows reach 1,152 keys (18
+    tiles: two splits of >= 8 tiles)."""
+    cfg = C.Config(1, 1, 2, 64, 8, 8, 3, 14, 17)
     r = G.Rollout(cfg, base_seed=4)
-    assert r.cache.attention_splits(64, 192 + 6 * 64 + 64) > 1
+    assert r.cache.attention_splits(64, 192 + 14 * 64 + 64) > 1
     r.run_first_chunk()
-    r.run_chunks(range(1, 9))
+    r.run_chunks(range(1, 17))
 
 
 def test_two_prompts_two_streams():
