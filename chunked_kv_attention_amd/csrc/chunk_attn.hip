@@ -526,18 +526,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= rows) return;
   const int c4 = threadIdx.x % TPR;
-  float mx = -INFINITY;
-  for (int j = 0; j < p.n_splits; ++j) mx = fmaxf(mx, p.part_lse[j * rows + row]);
+  // every split's log-sum-exp and values are loaded up front, so a thread has
+  // all its loads in flight at once
+  float lse[kAttnMaxSplits];
+  float4 v[kAttnMaxSplits];
+#pragma unroll
+  for (int j = 0; j < kAttnMaxSplits; ++j) {
+    const bool on = j < p.n_splits;
+    lse[j] = on ? p.part_lse[j * rows + row] : -INFINITY;
+    v[j] = on ? *reinterpret_cast<const float4*>(p.part_o + (j * rows + row) * D + 4 * c4)
+              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float mx = lse[0];
+#pragma unroll
+  for (int j = 1; j < kAttnMaxSplits; ++j) mx = fmaxf(mx, lse[j]);
   float wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < p.n_splits; ++j) {
-    const float w = __builtin_amdgcn_exp2f(p.part_lse[j * rows + row] - mx);
-    const float4 v = *reinterpret_cast<const float4*>(p.part_o + (j * rows + row) * D + 4 * c4);
+#pragma unroll
+  for (int j = 0; j < kAttnMaxSplits; ++j) {
+    if (j >= p.n_splits) break;
+    const float w = __builtin_amdgcn_exp2f(lse[j] - mx);
     wsum += w;
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+    acc.x += w * v[j].x;
+    acc.y += w * v[j].y;
+    acc.z += w * v[j].z;
+    acc.w += w * v[j].w;
   }
   const float inv = 1.f / wsum;
   const bf16x2 lo = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv)};

@@ -22,7 +22,7 @@ namespace {
 using ckv::bf16_t;
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxSplits = 4;
+constexpr int kMaxSplits = ckv::kAttnMaxSplits;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -111,6 +111,7 @@ constexpr int kConvChannelTile = 128;  // output channels per workgroup
 
 constexpr int kAttnQueryTile = 128;  // query rows per workgroup
 constexpr int kAttnKeyTile = 64;     // keys per LDS tile
+constexpr int kAttnMaxSplits = 4;    // most key splits of one call (partial-area size)
 
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s);
 hipError_t launch_text_store(const TextStoreParams& p, int head_dim, hipStream_t s);
