@@ -209,6 +209,21 @@ def test_config_rope_base_and_softmax_scale():
     print(f"theta 500, scale 0.2: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
 
 
+def test_reset_then_second_rollout():
+    """A cache reused after ckv_cache_reset: a second rollout with new inputs
+    matches a fresh oracle in every output, so no sink or ring entry of the
+    first rollout leaks into it."""
+    r = G.Rollout(TINY, base_seed=21)
+    r.run_first_chunk()
+    r.run_chunks(range(1, 6))
+    r.cache.reset()
+    r.oracle = O.OracleRollout(r.ocfg)
+    r.seed = 22
+    r.run_first_chunk()
+    r.run_chunks(range(1, 6))
+    print(f"after reset: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
+
+
 def test_window_membership_on_device():
     """K = 0 makes the softmax uniform, so the output is the mean of the
     window's V; with V = chunk id + 1 the output reveals exactly which chunks
