@@ -132,6 +132,35 @@ def _cross_over_padding(q, k_text, v_text, n_text, scale):
     return O.attend(q, k_text, v_text, scale)
 
 
+def _freqs_without_two(band_width, theta):
+    j = np.arange(band_width // 2, dtype=np.float64)
+    return np.power(float(theta), -j / float(band_width))
+
+
+def _angles_head_dim_normalised(positions, head_dim, theta):
+    dt, dh, dw = O.rope_bands(head_dim)
+    pos = np.asarray(positions, dtype=np.float64)
+    f = lambda n: np.power(float(theta), -2.0 * np.arange(n // 2) / float(head_dim))  # noqa: E731
+    return np.concatenate([np.outer(pos[:, 0], f(dt)), np.outer(pos[:, 1], f(dh)), np.outer(pos[:, 2], f(dw))], axis=1)
+
+
+def _first_step_reads_sink(self, layer, step, q, k, v, rows=None):
+    qr, kr = self.rotate(0, q), self.rotate(0, k)
+    ks, vs = kr, np.asarray(v, dtype=np.float64)
+    if layer in self.sink:
+        ks = np.concatenate([self.sink[layer][0], kr])
+        vs = np.concatenate([self.sink[layer][1], vs])
+    qr = qr if rows is None else qr[rows]
+    return O.attend(qr, ks, vs, self.cfg.scale), (qr, kr)
+
+
+def _first_step_records_sink(self, layer, step, q, k, v, rows=None):
+    qr, kr = self.rotate(0, q), self.rotate(0, k)
+    self.sink[layer] = (kr, np.asarray(v, dtype=np.float64))
+    qr = qr if rows is None else qr[rows]
+    return O.attend(qr, kr, v, self.cfg.scale), (qr, kr)
+
+
 MUTATIONS = [
     ("rope3d", _rope_sin_sign_flipped, [P.test_rope_is_complex_multiplication]),
     ("rope3d", _rope_half_split, [P.test_rope_is_complex_multiplication]),
@@ -152,6 +181,14 @@ MUTATIONS = [
     ("rms_norm", _norm_eps_outside_root, [P.test_qk_norm_constant_vector_closed_form]),
     ("cross_attention", _cross_over_padding, [P.test_cross_attention_uses_only_the_real_context_length]),
     ("rms_norm", _norm_sum_not_mean, [P.test_qk_norm_worked_example, P.test_qk_norm_unit_rms_scale_invariance_and_gain]),
+    ("band_frequencies", _freqs_without_two,
+     [lambda: P.test_band_frequencies_are_textbook_rope_of_the_band_width(128, 1e4),
+      lambda: P.test_each_band_is_1d_rope_when_other_coordinates_are_zero(128)]),
+    ("rope_angles", _angles_head_dim_normalised,
+     [lambda: P.test_each_band_is_1d_rope_when_other_coordinates_are_zero(128),
+      lambda: P.test_each_band_is_1d_rope_when_other_coordinates_are_zero(64)]),
+    ("OracleRollout.first_chunk_step", _first_step_reads_sink, [P.test_first_chunk_step_attends_to_its_own_chunk_only]),
+    ("OracleRollout.first_chunk_step", _first_step_records_sink, [P.test_first_chunk_step_attends_to_its_own_chunk_only]),
 ]
 
 
@@ -160,6 +197,10 @@ def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
     # sanity: the pins pass on the real oracle
     for pin in pins:
         assert not _fails(pin)
-    monkeypatch.setattr(O, name, mutant)
+    target = O
+    *owners, attr = name.split(".")
+    for owner in owners:  # a method of an oracle class, e.g. OracleRollout.first_chunk_step
+        target = getattr(target, owner)
+    monkeypatch.setattr(target, attr, mutant)
     caught = [_fails(pin) for pin in pins]
     assert all(caught), f"planted mistake in {name} ({mutant.__name__}) not caught by {caught}"

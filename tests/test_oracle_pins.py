@@ -114,6 +114,66 @@ def test_rope_band_layout(d):
         assert not changed[:lo].any() and not changed[hi:].any()
 
 
+def _library_inv_freq(dim, theta):
+    """Textbook RoPE frequencies from an independent library routine:
+    transformers' default rotary parameters (RoFormer's 1 / base^(2j/dim),
+    computed there in float32)."""
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding
+
+    cfg = LlamaConfig(hidden_size=dim, num_attention_heads=1, head_dim=dim,
+                      rope_parameters={"rope_type": "default", "rope_theta": float(theta)})
+    inv, _ = LlamaRotaryEmbedding.compute_default_rope_parameters(cfg)
+    return inv.double().numpy()
+
+
+def _roformer_freqs(dim, theta):
+    """RoFormer's frequencies written out pair by pair: theta_j = base^(-2j/dim)."""
+    return np.array([float(theta) ** (-2.0 * j / dim) for j in range(dim // 2)])
+
+
+def _rope_1d(x, pos, freqs):
+    """Textbook 1D rotary embedding over adjacent pairs (re, im): pair j of a
+    token at position p is multiplied by exp(i p w_j).  x [n, H, D]."""
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    z = z * np.exp(1j * np.outer(pos, freqs))[:, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("theta", [10000.0, 500.0])
+def test_band_frequencies_are_textbook_rope_of_the_band_width(d, theta):
+    """Each band's frequencies are the textbook RoPE frequencies of a head as
+    wide as the band ("3D RoPE" section: the frequency helper is called once
+    per band with the band's width): equal to a library routine's and to
+    RoFormer's formula written out."""
+    for width in O.rope_bands(d):
+        got = O.band_frequencies(width, theta)
+        np.testing.assert_allclose(got, _library_inv_freq(width, theta), rtol=1e-6)  # float32 there
+        np.testing.assert_allclose(got, _roformer_freqs(width, theta), rtol=1e-14)
+        assert got[0] == 1.0 and np.all(np.diff(got) < 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_each_band_is_1d_rope_when_other_coordinates_are_zero(d):
+    """With two of (f, h, w) zero, 3D RoPE is textbook 1D RoPE of the third
+    axis' band (frequencies from the library routine) and the identity on the
+    other two bands."""
+    dt, dh, dw = O.rope_bands(d)
+    edges = [(0, dt), (dt, dt + dh), (dt + dh, d)]
+    n = 9
+    x = _rand(n, 2, d)
+    for axis, (lo, hi) in enumerate(edges):
+        pos = np.zeros((n, 3), dtype=np.int64)
+        pos[:, axis] = np.arange(n) * 3 + 1          # up to 25, as far as the 5B grid reaches
+        ref = x.copy()
+        ref[:, :, lo:hi] = _rope_1d(x[:, :, lo:hi], pos[:, axis], _library_inv_freq(hi - lo, 1e4))
+        # float32 library frequencies: angle error <= 25 * 2^-24 relative
+        np.testing.assert_allclose(O.rope3d(x, pos, 1e4), ref, atol=2e-5)
+
+
 def test_rope_identity_at_origin_and_norm():
     x = _rand(5, 2, 128)
     np.testing.assert_array_equal(O.rope3d(x, np.zeros((5, 3)), 10000.0), x)
@@ -259,6 +319,40 @@ def test_rollout_window_assembly_tiny():
             ids = [-1] * 48 + [10 * j + s for j in O.window_chunks(c, 2) for _ in range(16)] + [tag] * 16
             assert vw[:, 0, 0].tolist() == [float(x) for x in ids]
             assert vw.shape[0] == O.window_key_count(c, 2, 4, 4, 3)
+
+
+def test_first_chunk_step_attends_to_its_own_chunk_only():
+    """Chunk 0's noisy steps come before every other chunk ("PhysisServe --
+    Wan2.2 5B", paragraph after "Inference profile"), so they see only their
+    own keys and record nothing.  Tagged values: a sink (V = -1) and a noisy
+    entry (V = -2) already exist in the oracle; the step's own V is 3
+    everywhere, so any other output means a foreign key was read.  With random
+    V the step equals the plain softmax over its own rotated keys at frames
+    0..F0-1, and a row subset equals those rows of the full result."""
+    cfg = O.OracleConfig(1, 2, 2, 64, 2, 4, 3, 2, 5)
+    ro = O.OracleRollout(cfg)
+    n0 = cfg.tokens(0)
+    ro.sink_pass(0, _rand(n0, 2, 64), _rand(n0, 2, 64), np.full((n0, 2, 64), -1.0))
+    ro.chunk_step(0, 1, 1, _rand(8, 2, 64), _rand(8, 2, 64), np.full((8, 2, 64), -2.0))
+    sink_k, sink_v = (a.copy() for a in ro.sink[0])
+    noisy_keys = sorted(ro.noisy)
+    q, k = _rand(n0, 2, 64), _rand(n0, 2, 64)
+    o, _ = ro.first_chunk_step(0, 1, q, k, np.full((n0, 2, 64), 3.0))
+    np.testing.assert_allclose(o, 3.0, rtol=1e-13)
+    np.testing.assert_array_equal(ro.sink[0][0], sink_k)
+    np.testing.assert_array_equal(ro.sink[0][1], sink_v)
+    assert sorted(ro.noisy) == noisy_keys
+    v = _rand(n0, 2, 64)
+    o, (qr, kr) = ro.first_chunk_step(0, 0, q, k, v)
+    pos = [(f, h, w) for f in range(3) for h in range(2) for w in range(4)]
+    bf = O.round_to_bf16
+    np.testing.assert_array_equal(kr, bf(O.rope3d(k, np.array(pos), 1e4)))
+    z = (qr[:, 0] @ kr[:, 0].T) / 8.0
+    p = np.exp(z - z.max(1, keepdims=True))
+    np.testing.assert_allclose(o[:, 0], (p / p.sum(1, keepdims=True)) @ v[:, 0], atol=1e-13)
+    rows = np.array([0, 5, n0 - 1])
+    o_rows, _ = ro.first_chunk_step(0, 0, q, k, v, rows=rows)
+    np.testing.assert_allclose(o_rows, o[rows], atol=1e-14)
 
 
 def test_rollout_chunk_step_matches_direct_definition():
