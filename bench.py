@@ -68,11 +68,12 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the QK-Norm append, cross-attention and copy lines (profiling runs: only the "
                          "rollout's launches are traced)")
-    ap.add_argument("--workload", choices=["rollout1", "rollout30x2", "attn880x19360", "conv88x160x384",
-                                           "conv44x80x384"], default="rollout1",
+    ap.add_argument("--workload", choices=["rollout1", "rollout30x2", "attn880x19360", "attn3x880x19360",
+                                           "conv88x160x384", "conv44x80x384"], default="rollout1",
                     help="rollout1: 1-layer 29-chunk rollout (default); rollout30x2: 30 layers x 2 prompts on "
-                         "2 streams; attn880x19360: the chunk-19 attention call alone, --steps times (for "
-                         "per-kernel counter runs); conv88x160x384 / conv44x80x384: one streaming causal Conv3d "
+                         "2 streams; attn880x19360: the peaky chunk-19 attention call alone, --steps times (for "
+                         "per-kernel counter runs); attn3x880x19360: the same call for 3 heads (one GPU's share "
+                         "of 8-way head sharding); conv88x160x384 / conv44x80x384: one streaming causal Conv3d "
                          "layer of the VAE decoder alone")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the counters file and exit")
@@ -320,60 +321,87 @@ def rollout30x2(args):
     print(json.dumps(result), flush=True)
 
 
-def attn880x19360(args):
-    """The 880-query x 19,360-key chunk-attention call on its own: a 1-layer
-    cache filled with the sink and chunks 1..19 at step 0 (seeded N(0,1)
-    inputs), then `--steps` timed calls of chunk 19's attention after
-    `--warmup` untimed ones.  Used for per-kernel counter runs, where the
-    rollout's mix of call shapes would blur the counters."""
+def single_call_timing(heads=24, calls=50, warmup=5, peaky=True):
+    """One chunk-attention call shape on its own: 880 queries x 19,360 keys
+    (chunk 19: sink 2640 + 18 x 880 window + 880 self), `heads` heads x 128.
+    A 1-layer cache gets the sink and chunks 1..19 at step 0 from seeded
+    N(0,1) bf16 inputs; with `peaky`, round(1% x 19,360) = 194 of the window's
+    key rows (a seeded permutation over all 19,360 positions) are scaled by 4
+    before RoPE, for a peaky softmax.  Then `calls` event-timed calls of chunk
+    19's attention on the launch stream after `warmup` untimed ones.
+    heads = 3 is one GPU's share of 24 heads sharded 8 ways."""
     import torch
 
     import chunked_kv_attention_amd as C
+    from chunked_kv_attention_amd import inputs as I
 
-    cfg = profile_config()
-    H, d = cfg.num_heads, cfg.head_dim
+    cfg = dataclasses.replace(profile_config(), num_steps=1, num_heads=heads)
+    d = cfg.head_dim
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
+    n0, n1 = cfg.tokens(0), cfg.tokens(1)
+    total = keys_of(cfg, 19)
+    rows = I.peaky_key_rows(total, 0.01, (7, heads, 19)) if peaky else []
 
     def rnd(n):
-        return torch.randn((n, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        return torch.randn((n, heads, d), generator=gen, device=dev, dtype=torch.float32)
+
+    def key_rows(chunk, k):
+        lo = 0 if chunk == 0 else n0 + n1 * (chunk - 1)
+        sel = [r - lo for r in rows if lo <= r < lo + k.shape[0]]
+        if sel:
+            k[torch.tensor(sel, device=dev)] *= 4.0
+        return k.to(torch.bfloat16)
 
     cache = C.Cache(cfg)
-    n0, n1 = cfg.tokens(0), cfg.tokens(1)
-    q0 = rnd(n0)
-    cache.sink_build(0, q0, rnd(n0), rnd(n0), torch.empty_like(q0))
-    q_rot = torch.empty((n1, H, d), device=dev, dtype=torch.bfloat16)
+    q0 = rnd(n0).to(torch.bfloat16)
+    cache.sink_build(0, q0, key_rows(0, rnd(n0)), rnd(n0).to(torch.bfloat16), torch.empty_like(q0))
+    q_rot = torch.empty((n1, heads, d), device=dev, dtype=torch.bfloat16)
     for c in range(1, 20):
-        cache.rope_append(0, 0, c, rnd(n1), rnd(n1), rnd(n1), q_rot)
+        cache.rope_append(0, 0, c, rnd(n1).to(torch.bfloat16), key_rows(c, rnd(n1)), rnd(n1).to(torch.bfloat16),
+                          q_rot)
     out = torch.empty_like(q_rot)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         cache.chunk_attention(0, 0, 19, q_rot, out, stream=stream)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(calls):
         cache.chunk_attention(0, 0, 19, q_rot, out, stream=stream)
     stop.record(stream)
     torch.cuda.synchronize()
-    us = 1e3 * start.elapsed_time(stop) / args.steps
+    us = 1e3 * start.elapsed_time(stop) / calls
     flops = attn_flops(cfg, 19)
     tflops = flops / (us * 1e-6) / 1e12
+    return {"us_per_call": round(us, 2), "tflops": round(tflops, 2),
+            "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "launches_timed": calls,
+            "key_splits": cache.attention_splits(n1, total), "heads": heads,
+            "inputs": ("N(0,1) bf16; 194 of the 19,360 window key rows scaled x4 before RoPE (peaky softmax)"
+                       if peaky else "N(0,1) bf16")}
+
+
+def attn880x19360(args, heads=24):
+    """`--workload attn880x19360` (24 heads) / `attn3x880x19360` (3 heads):
+    the single peaky 880-query x 19,360-key call alone, `--steps` timed calls
+    (also used for per-kernel counter runs, where the rollout's mix of call
+    shapes would blur the counters)."""
+    r = single_call_timing(heads, calls=args.steps, warmup=args.warmup)
     print(json.dumps({
         "metric": "chunk-attn TFLOP/s, 880 queries x 19,360 keys",
-        "value": round(tflops, 2),
+        "value": r["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "us_per_call": round(us, 2),
+        "us_per_call": r["us_per_call"],
         "higher_is_better": True,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "one chunk-attention call: 880 queries x 19,360 keys (sink + 18 chunks + self), "
-                               "24 heads x 128", "key_splits": cache.attention_splits(n1, 19360)},
-        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": f"one chunk-attention call: 880 queries x 19,360 keys (sink + 18 chunks + self), "
+                               f"{heads} heads x 128", "inputs": r["inputs"], "key_splits": r["key_splits"]},
+        "pct_bf16_peak": r["pct_bf16_peak"],
     }), flush=True)
 
 
@@ -535,6 +563,9 @@ def main():
     if args.workload == "attn880x19360":
         attn880x19360(args)
         return
+    if args.workload == "attn3x880x19360":
+        attn880x19360(args, heads=3)
+        return
     if args.workload in CONV_LAYERS:
         conv_workload(args)
         return
@@ -641,7 +672,8 @@ def main():
             "algorithmic_tflop_per_step": round(total_flops / 1e12, 4),
         },
         "pct_bf16_peak": round(100 * total_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "chunk_attn_880x19360": {
+        "chunk_attn_880x19360_in_rollout": {
+            "inputs": "N(0,1) bf16 (the rollout's own chunks 19..28)",
             "us_per_call": round(big_us, 2),
             "tflops": round(big_tflops, 2),
             "pct_bf16_peak": round(100 * big_tflops / PEAK_BF16_TFLOPS, 2),
@@ -668,6 +700,10 @@ def main():
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         },
     }
+    # the single call as stated for the 880 x 19,360 shape (peaky keys), and the
+    # 3-head share of 8-way head sharding (4 key splits)
+    result["chunk_attn_880x19360"] = single_call_timing(24)
+    result["chunk_attn_880x19360_3heads"] = single_call_timing(3)
     if not args.no_extras:
         result["norm_rope_append_880"], result["device_copy_same_bytes"] = norm_append_and_copy(
             C, cfg, dev, stream, inputs, calls)

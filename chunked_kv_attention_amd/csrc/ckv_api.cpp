@@ -1,10 +1,11 @@
 // C-ABI of the same-step chunk attention library (declared in include/ckv.h).
 //
 // Host responsibilities: validate every call against the config and the
-// schedule (ring_index.hpp), lay out the caller's arena, build the RoPE angle
-// tables in float64 once and round them to float32, turn a window into at
-// most three key runs, pick the key-split count, and launch the kernels on
-// the caller's stream.  Nothing here allocates device memory or synchronises.
+// schedule (ring_index.hpp), lay out the caller's arena, have the RoPE angle
+// tables built once on the device (float64, rounded once to float32), turn a
+// window into at most three key runs, pick the key-split count, and launch
+// the kernels on the caller's stream.  Nothing here allocates device memory,
+// copies from the host or synchronises.
 #include "ckv.h"
 
 #include <hip/hip_runtime_api.h>
@@ -100,8 +101,7 @@ struct ckv_cache {
   size_t arena_bytes;
   Layout L;
   ckv::Schedule sched;
-  std::vector<float> tables;  // float2 (cos, sin), rounded once from float64
-  bool tables_uploaded;
+  bool tables_built;  // the angle tables are built in the arena on the first device call
   int num_cus;
   std::vector<int> text_len;  // per layer: context rows stored (0 = none)
 
@@ -109,28 +109,7 @@ struct ckv_cache {
       : cfg(c), dry(is_dry), arena(a), arena_bytes(bytes), L(layout_of(&c)),
         sched(c.num_layers, c.num_steps, c.window_chunks, c.max_chunks, c.first_chunk_frames * c.grid_h * c.grid_w,
               c.grid_h * c.grid_w),
-        tables_uploaded(false), num_cus(0), text_len(c.num_layers, 0) {}
-
-  // 3D RoPE angle tables ("Learning Video Generation from the Wan2.2 Source
-  // Code", Chapter 4, "3D RoPE"): per band of width D, pair j rotates by
-  // pos * theta^(-2j/D); cos and sin are evaluated in float64 and rounded
-  // once to float32.
-  void build_tables() {
-    const Bands b = bands_of(cfg.head_dim);
-    tables.clear();
-    auto band = [&](int positions, int width) {
-      for (int p = 0; p < positions; ++p)
-        for (int j = 0; j < width / 2; ++j) {
-          const double w = std::pow(cfg.rope_theta, -2.0 * j / (double)width);
-          const double a = (double)p * w;
-          tables.push_back((float)std::cos(a));
-          tables.push_back((float)std::sin(a));
-        }
-    };
-    band(L.frames_table, b.t);
-    band(cfg.grid_h, b.h);
-    band(cfg.grid_w, b.w);
-  }
+        tables_built(false), num_cus(0), text_len(c.num_layers, 0) {}
 
   bf16_t* sink_k(int layer) const { return (bf16_t*)(arena + L.sink_off + L.sink_layer_bytes * layer); }
   bf16_t* sink_vt(int layer) const { return sink_k(layer) + (size_t)cfg.num_heads * L.n0 * cfg.head_dim; }
@@ -167,11 +146,23 @@ ckv_status ensure_device(ckv_cache* c, hipStream_t s) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return CKV_E_HIP;
     c->num_cus = cus > 0 ? cus : 256;
   }
-  if (!c->tables_uploaded) {
-    if (hipMemcpyAsync(c->arena + c->L.tables_off, c->tables.data(), c->tables.size() * sizeof(float),
-                       hipMemcpyHostToDevice, s) != hipSuccess)
-      return CKV_E_HIP;
-    c->tables_uploaded = true;
+  if (!c->tables_built) {
+    // 3D RoPE angle tables ("Learning Video Generation from the Wan2.2 Source
+    // Code", Chapter 4, "3D RoPE"): per band of width D, pair j rotates by
+    // pos * theta^(-2j/D); built by a kernel on the call's stream, so the
+    // first call stays asynchronous like every other.
+    const Bands b = bands_of(c->cfg.head_dim);
+    ckv::RopeTableParams t;
+    t.out = (float2*)(c->arena + c->L.tables_off);
+    t.frames = c->L.frames_table;
+    t.grid_h = c->cfg.grid_h;
+    t.grid_w = c->cfg.grid_w;
+    t.band_t = b.t;
+    t.band_h = b.h;
+    t.band_w = b.w;
+    t.theta = c->cfg.rope_theta;
+    if (ckv::launch_rope_table(t, s) != hipSuccess) return CKV_E_HIP;
+    c->tables_built = true;
   }
   return CKV_OK;
 }
@@ -286,7 +277,6 @@ ckv_status ckv_cache_create(const ckv_config* cfg, void* device_arena, size_t ar
     return CKV_E_ARENA;
   ckv_cache* c = new (std::nothrow) ckv_cache(*cfg, false, (char*)device_arena, arena_bytes);
   if (!c) return CKV_E_INVALID;
-  c->build_tables();
   *out = c;
   return CKV_OK;
 }

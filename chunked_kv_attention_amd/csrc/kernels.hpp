@@ -35,6 +35,16 @@ struct RopeAppendParams {
   float eps;
 };
 
+// RoPE angle tables of a cache: float2 (cos, sin) per band pair and position,
+// time band [frames][band_t/2], then height [grid_h][band_h/2], then width
+// [grid_w][band_w/2], from float64 angles rounded once to float32.
+struct RopeTableParams {
+  float2* out;
+  int frames, grid_h, grid_w;
+  int band_t, band_h, band_w;  // widths in dims
+  double theta;
+};
+
 // The text context of one layer into the attention store: K rows
 // [H][max_text][d] and V^T [H][d][max_text], V^T columns past n_text zeroed.
 struct TextStoreParams {
@@ -114,6 +124,7 @@ constexpr int kAttnKeyTile = 64;     // keys per LDS tile
 constexpr int kAttnMaxSplits = 4;    // most key splits of one call (partial-area size)
 
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s);
+hipError_t launch_rope_table(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_text_store(const TextStoreParams& p, int head_dim, hipStream_t s);
 hipError_t launch_chunk_attention(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_copy_kv(const CopyKVParams& p, int head_dim, hipStream_t s);

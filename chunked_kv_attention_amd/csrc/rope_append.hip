@@ -6,9 +6,11 @@
 // height and width bands of 2(d/6) dims each; every adjacent pair
 // (x[2p], x[2p+1]) is a complex number multiplied by e^{i * pos * w}, where
 // pos is the token's frame, patch row or patch column for the pair's band.
-// q and k are rotated, v is not.  The cos/sin values come from tables built
-// on the host in float64 and rounded once to float32; the rotation itself is
-// float32 with one bf16 rounding (nearest-even) at the end.
+// q and k are rotated, v is not.  The cos/sin values come from tables that
+// rope_table_kernel builds once per cache in float64 (w_j = theta^(-2j/D_band)
+// per band, the band's own width, then cos and sin of pos * w_j) and rounds
+// once to float32; the rotation itself is float32 with one bf16 rounding
+// (nearest-even) at the end.
 //
 // QK-Norm ("Learning Video Generation from the Wan2.2 Source Code", Chapter 4,
 // "3D RoPE" detail paragraph: q and k each pass an RMSNorm after their linear
@@ -270,6 +272,24 @@ __global__ __launch_bounds__(kThreads) void text_store_kernel(TextStoreParams p,
   }
 }
 
+// The angle tables: (cos, sin) float2 for [frames][Pt] | [grid_h][Ph] |
+// [grid_w][Pw] pairs, evaluated in float64 and rounded once to float32.
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTableParams p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int nt = p.frames * (p.band_t / 2), nh = p.grid_h * (p.band_h / 2), nw = p.grid_w * (p.band_w / 2);
+  if (i >= nt + nh + nw) return;
+  int pos, j, width;
+  if (i < nt) {
+    pos = i / (p.band_t / 2), j = i % (p.band_t / 2), width = p.band_t;
+  } else if (i < nt + nh) {
+    pos = (i - nt) / (p.band_h / 2), j = (i - nt) % (p.band_h / 2), width = p.band_h;
+  } else {
+    pos = (i - nt - nh) / (p.band_w / 2), j = (i - nt - nh) % (p.band_w / 2), width = p.band_w;
+  }
+  const double a = (double)pos * pow(p.theta, -2.0 * j / (double)width);
+  p.out[i] = make_float2((float)cos(a), (float)sin(a));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void copy_kv_kernel(CopyKVParams p) {
   const long long total = (long long)p.n_tokens * p.num_heads * D;
@@ -315,6 +335,13 @@ hipError_t launch_text_store(const TextStoreParams& p, int head_dim, hipStream_t
     hipLaunchKernelGGL(text_store_kernel<64>, grid, dim3(kThreads), 0, s, p, k_blocks);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const RopeTableParams& p, hipStream_t s) {
+  const int n = p.frames * (p.band_t / 2) + p.grid_h * (p.band_h / 2) + p.grid_w * (p.band_w / 2);
+  if (n <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -97,8 +97,9 @@ size_t ckv_cache_bytes(const ckv_config* cfg);
 
 /* Create a cache over a caller-owned device arena of at least
  * ckv_cache_bytes(cfg) bytes, 256-byte aligned.  Host-only: touches no device
- * memory (the angle tables are uploaded by the first rope_append/sink_build,
- * on that call's stream).  Sink and ring layout inside the arena:
+ * memory.  The RoPE angle tables are built in the arena by a small kernel
+ * enqueued on the stream of the cache's first device call (no host-to-device
+ * copy, so that call does not block the host either).  Sink and ring layout inside the arena:
  *   sink  K [L][H][F0*gh*gw][d],  V transposed [L][H][d][F0*gh*gw];
  *   rings K [L][S][H][(W+1)*gh*gw][d], V transposed [L][S][H][d][(W+1)*gh*gw];
  *   text  K [L][H][CKV_MAX_TEXT_TOKENS][d], V transposed [L][H][d][CKV_MAX_TEXT_TOKENS].
@@ -166,7 +167,11 @@ ckv_status ckv_norm_sink_build(ckv_cache* c, int32_t layer, const void* q, const
                                const void* v, const float* q_gain, const float* k_gain, float eps,
                                void* q_rot, void* stream);
 
-/* Chunk attention: out = softmax(scale * q_rot K_win^T) V_win per head, no
+/* Chunk attention ("PhysisServe -- Wan2.2 5B" model card, "Inference
+ * profile" table, KV-history row, and the paragraph after the table: a
+ * chunk's queries see the clean first-chunk sink, at most W earlier chunks'
+ * K/V from the same denoising step, chunk 0 never twice, and its own K/V):
+ * out = softmax(scale * q_rot K_win^T) V_win per head, no
  * mask, with K_win/V_win gathered in place from
  *   chunk == 0, step in [0,S): the chunk's own step-`step` K/V (needs that
  *               append to be the last write to the sink area; CKV_E_STATE);
@@ -202,7 +207,9 @@ ckv_status ckv_text_store(ckv_cache* c, int32_t layer, const void* k_text, const
 ckv_status ckv_cross_attention(ckv_cache* c, int32_t layer, int32_t chunk, const void* q,
                                void* out, void* stream);
 
-/* Host-only: the window (layer, step, chunk) attends to, as <= 3 segments in
+/* Host-only: the window (layer, step, chunk) attends to (model card,
+ * "Inference profile" table, KV-history row: the sink plus at most W of the
+ * most recent earlier chunks, chunk 0 only as the sink), as <= 3 segments in
  * key order (sink area, then up to two runs of ring slots; the last run ends
  * with the chunk itself).  Depends only on the config.  *n_segs receives the
  * count; CKV_E_INVALID if max_segs is too small or an index is out of range. */

@@ -77,10 +77,19 @@ def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
 class Rollout:
     """Runs chunks through one cache on the GPU and through the oracle, on the
     same seeded bf16 inputs, and compares each attention output (all rows, or
-    a sample of rows when `rows_per_call` is set)."""
+    a sample of rows when `rows_per_call` is set).
 
-    def __init__(self, cfg: C.Config, base_seed=0, prompt=0, rows_per_call=None, stream=None, also_f64=False,
-                 qk_norm=None):
+    Every output is held to the bar twice: against the oracle that hands the
+    rotated q/k to attention in bf16 (the backbone's precision), and against
+    the unrounded float64 chain (the rotation's own precision); both must
+    stay within max |diff| <= 2e-2 and relative L2 <= 5e-3.  With
+    `f64_bar=False` (inputs whose keys are scaled x4, where the bf16 rounding
+    of the rotated keys alone moves the float64 result by about the bar) the
+    second comparison allows the distance between the two oracles on top of
+    the bar instead."""
+
+    def __init__(self, cfg: C.Config, base_seed=0, prompt=0, rows_per_call=None, stream=None, also_f64=True,
+                 qk_norm=None, f64_bar=True):
         self.cfg = cfg
         # optional QK-Norm in front of the rotation: (q_gain, k_gain, eps), gains float32 [H*d]
         self.qk_norm = qk_norm
@@ -91,9 +100,11 @@ class Rollout:
                                    cfg.grid_w, cfg.first_chunk_frames, cfg.window_chunks, cfg.max_chunks,
                                    cfg.rope_theta, cfg.softmax_scale)
         self.oracle = O.OracleRollout(self.ocfg)
-        # optional second oracle that keeps rotated q/k unrounded (reported, not asserted)
+        # second oracle that keeps rotated q/k unrounded (asserted like the first)
         self.oracle64 = O.OracleRollout(dataclasses.replace(self.ocfg, attention_inputs="f64")) if also_f64 else None
         self.worst64 = (0.0, 0.0)
+        self.f64_bar = f64_bar
+        self.worst_pair = (0.0, 0.0)  # bf16-input oracle against the float64 chain
         self.seed = base_seed
         self.prompt = prompt
         self.rows_per_call = rows_per_call
@@ -165,10 +176,20 @@ class Rollout:
         got = from_dev(out_dev)
         if rows is not None:
             got = got[rows]
+        what = f"{kind} layer {layer} step {step} chunk {chunk}"
         if self.oracle64 is not None:
-            e64 = attn_errors(got, refs[1])
+            if self.f64_bar:
+                e64 = assert_attn_close(got, refs[1], what + " (against unrounded float64 q/k)")
+            else:
+                # the two oracles themselves differ by the bf16 rounding of the
+                # rotated q/k; the GPU may be that far from the float64 chain
+                # plus the bar, no further
+                pair = attn_errors(ref, refs[1])
+                e64 = attn_errors(got, refs[1])
+                self.worst_pair = (max(self.worst_pair[0], pair[0]), max(self.worst_pair[1], pair[1]))
+                assert e64[0] <= pair[0] + MAX_ABS and e64[1] <= pair[1] + REL_L2, (what, e64, pair)
             self.worst64 = (max(self.worst64[0], e64[0]), max(self.worst64[1], e64[1]))
-        errs = assert_attn_close(got, ref, f"{kind} layer {layer} step {step} chunk {chunk}")
+        errs = assert_attn_close(got, ref, what)
         self.worst = (max(self.worst[0], errs[0]), max(self.worst[1], errs[1]))
         return errs
 

@@ -218,6 +218,7 @@ def test_reset_then_second_rollout():
     r.run_chunks(range(1, 6))
     r.cache.reset()
     r.oracle = O.OracleRollout(r.ocfg)
+    r.oracle64 = O.OracleRollout(dataclasses.replace(r.ocfg, attention_inputs="f64"))
     r.seed = 22
     r.run_first_chunk()
     r.run_chunks(range(1, 6))
@@ -256,36 +257,71 @@ def test_bootstrap_first_chunk_profile():
     print(f"bootstrap worst: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
 
 
-def test_single_chunk_880x19360_peaky():
-    """Chunk 19 at one step: sink 2640 + 18 x 880 window + 880 self = 19,360
-    keys; 1% of the window's keys scaled x4 before RoPE (peaky softmax)."""
-    cfg = C.Config(1, 1, 24, 128, 22, 40, 3, 18, 29)
-    r = G.Rollout(cfg, base_seed=11, rows_per_call=64, also_f64=True)
+def _peaky_window_up_to_chunk_19(r, seed):
+    """Sink + chunks 1..18 recorded unchecked, then chunk 19 checked: its
+    window is 2640 + 18 x 880 + 880 = 19,360 keys, and 1% of them (194 rows,
+    a seeded permutation over the whole window) are scaled x4 before RoPE
+    (peaky softmax)."""
     total = 2640 + 18 * 880 + 880
-    peaky = I.peaky_key_rows(total, 0.01, (11, 0, 0))
+    peaky = I.peaky_key_rows(total, 0.01, (seed, 0, 0))
     assert len(peaky) == 194
-    offsets = [0, 2640] + [2640 + 880 * j for j in range(1, 20)]
 
     def rows_of(chunk):
         lo = 0 if chunk == 0 else 2640 + 880 * (chunk - 1)
         hi = lo + (2640 if chunk == 0 else 880)
         return peaky[(peaky >= lo) & (peaky < hi)] - lo
-    assert offsets[-1] == total
     r.step("sink", 0, 0, 0, scale_rows=rows_of(0), check=False)
     for c in range(1, 19):
         r.step("chunk", 0, 0, c, scale_rows=rows_of(c), check=False)
-    mx, rl2 = r.step("chunk", 0, 0, 19, scale_rows=rows_of(19))
-    splits = r.cache.attention_splits(880, total)
+    return r.step("chunk", 0, 0, 19, scale_rows=rows_of(19))
+
+
+def test_single_chunk_880x19360_peaky():
+    """Chunk 19 at one step: sink 2640 + 18 x 880 window + 880 self = 19,360
+    keys; 1% of the window's keys scaled x4 before RoPE (peaky softmax)."""
+    cfg = C.Config(1, 1, 24, 128, 22, 40, 3, 18, 29)
+    r = G.Rollout(cfg, base_seed=11, rows_per_call=64, f64_bar=False)
+    mx, rl2 = _peaky_window_up_to_chunk_19(r, 11)
+    splits = r.cache.attention_splits(880, 19360)
     print(f"880x19360 peaky: max abs {mx:.3e} rel L2 {rl2:.3e} (splits {splits}); against "
-          f"unrounded float64 q/k: max abs {r.worst64[0]:.3e} rel L2 {r.worst64[1]:.3e}")
+          f"unrounded float64 q/k: max abs {r.worst64[0]:.3e} rel L2 {r.worst64[1]:.3e} (the two oracles "
+          f"differ by {r.worst_pair[0]:.3e} / {r.worst_pair[1]:.3e})")
     assert splits > 1  # the split-key path and its merge are exercised
+
+
+def test_four_key_splits_three_heads_880x19360():
+    """One GPU's share of 24 heads sharded 8 ways ("Learning Video Generation
+    from the Wan2.2 Source Code", Ch.8, Ulysses: split heads, not the
+    sequence): 3 heads x 880 queries x 19,360 keys, which fills the chip only
+    with 4 key splits.  Chunk 19 (peaky) and chunk 20 (its ring window wraps
+    into two runs), sampled rows."""
+    cfg = C.Config(1, 1, 3, 128, 22, 40, 3, 18, 29)
+    r = G.Rollout(cfg, base_seed=13, rows_per_call=128, f64_bar=False)
+    assert r.cache.attention_splits(880, 19360) == 4
+    mx, rl2 = _peaky_window_up_to_chunk_19(r, 13)
+    mx20, rl20 = r.step("chunk", 0, 0, 20)
+    print(f"3 heads x 880 x 19360, 4 splits: chunk 19 max abs {mx:.3e} rel L2 {rl2:.3e}; chunk 20 max abs "
+          f"{mx20:.3e} rel L2 {rl20:.3e}; unrounded float64 q/k worst {r.worst64[0]:.3e} / {r.worst64[1]:.3e} "
+          f"(oracles differ by {r.worst_pair[0]:.3e} / {r.worst_pair[1]:.3e})")
+
+
+def test_four_key_splits_every_element():
+    """2 heads x 64, 8 x 16 grid, window 14: from chunk 15 on the window holds
+    384 + 14 x 128 + 128 = 2,304 keys (36 tiles), run as 4 key splits; every
+    output element of every call against the oracle."""
+    cfg = C.Config(1, 1, 2, 64, 8, 16, 3, 14, 17)
+    r = G.Rollout(cfg, base_seed=6)
+    assert r.cache.attention_splits(128, 2304) == 4
+    r.run_first_chunk()
+    r.run_chunks(range(1, 17))
+    print(f"4-split d=64: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
 
 
 @pytest.mark.timeout(600)
 def test_rollout_one_layer_profile():
     """29 chunks x 4 steps, 24 x 128, 880 tokens per chunk after the 2640-token
     first chunk; W = 18 so the window grows, then evicts.  Sampled rows."""
-    r = G.Rollout(PROFILE1, base_seed=5, rows_per_call=12, also_f64=True)
+    r = G.Rollout(PROFILE1, base_seed=5, rows_per_call=12)
     r.run_first_chunk()
     r.run_chunks(range(1, 29), progress=True)
     print(f"1-layer rollout worst: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}; against unrounded "

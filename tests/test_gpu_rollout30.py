@@ -88,22 +88,24 @@ def test_rollout_30_layers_two_prompts_two_streams():
             print(f"  enqueued chunk {c}", flush=True)
     torch.cuda.synchronize()
     print(f"rollout done; checking {len(sample)} sampled calls", flush=True)
-    ocfg = O.OracleConfig(30, 4, 24, 128, 22, 40, 3, 18, 29)
     worst = (0.0, 0.0)
+    host = lambda ts: [G.from_dev(t) for t in ts]  # noqa: E731
     for prompt, layer, chunk, step in sample:
-        ro = O.OracleRollout(ocfg)
-        host = lambda ts: [G.from_dev(t) for t in ts]  # noqa: E731
-        q0, k0, v0 = host(_draw(prompt, layer, 0, SINK_STEP))
-        ro.sink_pass(layer, q0, k0, v0, rows=np.array([0]))
-        for j in O.window_chunks(chunk, 18):
-            _, kj, vj = host(_draw(prompt, layer, j, step))
-            ro.noisy[(layer, step, j)] = (ro.rotate(j, kj), vj)
-        q, k, v = host(_draw(prompt, layer, chunk, step))
         rows = G.sample_rows(n1, 24, seed=prompt * 1000 + layer * 10 + chunk)
-        ref, _ = ro.chunk_step(layer, step, chunk, q, k, v, rows=rows)
         got = G.from_dev(kept[(prompt, layer, chunk, step)])[rows]
-        mx, rl2 = G.assert_attn_close(got, ref, f"prompt {prompt} layer {layer} chunk {chunk} step {step}")
-        worst = (max(worst[0], mx), max(worst[1], rl2))
+        q0, k0, v0 = host(_draw(prompt, layer, 0, SINK_STEP))
+        win = {j: host(_draw(prompt, layer, j, step))[1:] for j in O.window_chunks(chunk, 18)}
+        q, k, v = host(_draw(prompt, layer, chunk, step))
+        # the rotated q/k handed to attention in bf16, then unrounded float64
+        for inputs in ("bf16", "f64"):
+            ro = O.OracleRollout(O.OracleConfig(30, 4, 24, 128, 22, 40, 3, 18, 29, attention_inputs=inputs))
+            ro.sink_pass(layer, q0, k0, v0, rows=np.array([0]))
+            for j, (kj, vj) in win.items():
+                ro.noisy[(layer, step, j)] = (ro.rotate(j, kj), vj)
+            ref, _ = ro.chunk_step(layer, step, chunk, q, k, v, rows=rows)
+            mx, rl2 = G.assert_attn_close(got, ref, f"prompt {prompt} layer {layer} chunk {chunk} step {step} ({inputs})")
+            if inputs == "bf16":
+                worst = (max(worst[0], mx), max(worst[1], rl2))
         print(f"  prompt {prompt} layer {layer} chunk {chunk} step {step}: max abs {mx:.2e} rel L2 {rl2:.2e}",
               flush=True)
     assert n0 == 2640
