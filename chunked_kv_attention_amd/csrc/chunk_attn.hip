@@ -20,31 +20,32 @@
 // buffers alternate; tile t+1 is in flight while tile t is computed, with
 // one barrier per tile.
 //
-// Products use v_mfma_f32_16x16x32_bf16 (16x16 output blocks): per tile and
-// wave
-//   S^T[64 keys x 32 queries] = K_tile Q^T      8 independent 16x16 blocks
-//   O^T[d x 32 queries]      += V^T_tile P^T    2d/16 independent blocks
-// so both products keep many accumulation chains in flight.  With the
-// queries as the N columns, a lane holds 16 scores of each of its 2 queries;
-// a query's row max needs a 4-lane exchange (lane xor 16, xor 32).  K rows
-// sit in LDS in a permuted order chosen so that the 8 scores a lane holds
-// for each 32-key step of the PV product are 8 consecutive keys, so P goes
-// from registers straight into the B operand.
+// Products use v_mfma_f32_32x32x16_bf16 (32x32 output blocks; on gfx950 it
+// does twice the work of the 16x16x32 form in the same issue time, which
+// caps that form at half the matrix peak): per tile and wave
+//   S^T[64 keys x 32 queries] = K_tile Q^T      2 blocks x d/16 steps
+//   O^T[d x 32 queries]      += V^T_tile P^T    d/32 blocks x 4 steps
+// With the queries as the N columns, lane l holds the scores of query l % 32
+// for 32 of the tile's 64 keys (lanes l and l + 32 share a query).  K rows
+// sit in LDS in a permuted order (bits 2 and 3 of the row index swapped) so
+// that the 8 consecutive scores a lane holds for each 16-key step of the PV
+// product are 8 consecutive keys: P goes from registers straight into the B
+// operand.
 //
 // Softmax.  Scores stay raw; the scale (times log2 e) is folded into one FMA
 // per score before exp2.  The running max is lazy: O and the running sums are
 // rescaled only when a tile raises some row's max by more than 2^8 (a
 // wave-uniform branch), otherwise the stale max is kept and P may reach 256,
 // which bf16 and the fp32 accumulators hold exactly enough.  The test needs
-// no cross-lane max: each lane compares its own raw scores of a query with
-// that query's threshold (m + 8) / (scale log2 e), and the 4-lane max is
+// no cross-lane max: each lane compares its own raw scores of its query with
+// that query's threshold (m + 8) / (scale log2 e), and the 2-lane max is
 // taken only inside the rare rescale branch.  The row sums add the same
 // bf16-rounded P that multiplies V (v_dot2_f32_bf16 against ones), so
 // numerator and denominator see the same weights.
 //
 // Occupancy.  880 queries x 24 heads is only 168 workgroups of 128 rows for
-// 256 CUs, so the key range is split into up to 4 parts when that fills the
-// chip better; each part writes normalised fp32 partials and a log2-domain
+// 256 CUs (21 for a 3-head share), so the key range is split into as many
+// parts as fill the chip's workgroup slots once (3 and 24 parts there); each part writes normalised fp32 partials and a log2-domain
 // log-sum-exp, and a second kernel merges them (softmax over a concatenation
 // equals the LSE-weighted merge of per-part softmaxes).
 //
@@ -62,6 +63,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int QT = kAttnQueryTile;  // 128
@@ -70,8 +72,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
-constexpr int KB = KT / 16;           // 16-key blocks of S^T per tile
-constexpr int KS = KT / 32;           // 32-key steps of the PV product per tile
+constexpr int MB = KT / 32;           // 32-key blocks of S^T per tile
+constexpr int KS = KT / 16;           // 16-key steps of the PV product per tile
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
@@ -98,19 +100,26 @@ __device__ inline int swz(int r) {
   return Chunks == 16 ? (r & 15) : ((r >> 1) & 7);
 }
 
-// K rows sit in LDS in a permuted order: LDS row p = 32s + 16b + 4h + i holds
-// tile key 32s + 8h + 4b + i.  MFMA block kb = 2s + b then reads LDS rows
-// 16kb .. 16kb+15, and the lane group h gets keys 32s + 8h + 4b + (0..3).
-__device__ inline int key_of_lds_row(int p) { return (p & ~31) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3); }
+// K rows sit in LDS in a permuted order: LDS row p holds tile key p with
+// bits 2 and 3 swapped.  S^T block mb then gives lane l (h = l / 32) the
+// scores of LDS rows 32mb + 8g + 4h + e (g, e = 0..3), i.e. of tile keys
+// 32mb + 16(g/2) + 8h + 4(g%2) + e: for PV step ks = 2mb + g/2 its eight
+// scores 8(g/2) .. 8(g/2)+7 are keys 16ks + 8h .. 16ks + 8h + 7, the B
+// operand's k-range for that lane.
+__device__ inline int key_of_lds_row(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
 __device__ inline bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
-// max over the 4 lanes l, l^16, l^32, l^48 that share a query
-__device__ inline float quad_max(float x) {
+// Max and sum of x over the lane pair l, l ^ 32 that shares a query.  After
+// the swap one result holds x[l] and the other x[l ^ 32] in every lane (in
+// either order), so both lanes compute the same value bit for bit.
+__device__ inline float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // max of finite floats without the quieting of NaN inputs that fmaxf implies
@@ -299,121 +308,117 @@ __device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, 
   }
 }
 
-// One key tile for a wave's 32 queries (2 blocks of 16):
+// One key tile for a wave's 32 queries:
 //   S^T = K_tile Q^T, online softmax per query, O^T += V^T_tile P^T.
-// S value (kb, qb)[i] is the score of tile key 32s + 8h + 4b + i (kb = 2s + b,
-// h = lane / 16) for query 16qb + lane % 16.  O value (db, qb)[i] is head dim
-// 16db + 4h + i of that query.  ka[kk] / va[ks] are this lane's operand byte
-// offsets within a K / V^T tile for 32-dim step kk / 32-key step ks.
+// S value (mb)[r] is the score of tile key 32mb + 16(r/8) + 8h + 4((r/4)%2)
+// + r%4 (h = lane / 32) for query lane % 32.  O value (db)[r] is head dim
+// 32db + 8(r/4) + 4h + r%4 of that query.  ka[kk] / va[ks] are this lane's
+// operand byte offsets within a K / V^T tile for 16-dim step kk / 16-key
+// step ks.
 template <int D>
-__device__ inline void attend_tile(const char* sk, const char* sv, const int (&ka)[D / 32], const int (&va)[KS],
-                                   const bf16x8 (&qf)[D / 32][2], f32x4 (&o)[D / 16][2], float (&m)[2],
-                                   float (&thr)[2], float (&lsum)[2], float scale_log2, bool masked, int t0, int key_end, int h) {
+__device__ inline void attend_tile(const char* sk, const char* sv, const int (&ka)[D / 16], const int (&va)[KS],
+                                   const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], float& m, float& thr, float& lsum,
+                                   float scale_log2, bool masked, int t0, int key_end, int h) {
   using T = Tile<D>;
-  constexpr int KK = D / 32;
-  constexpr int DB = D / 16;
-  f32x4 s[KB][2];
+  constexpr int KK = D / 16;
+  constexpr int DB = D / 32;
+  f32x16 s[MB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sk + kb * 16 * T::kRowBytesK + ka[kk]));
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk][qb], s[kb][qb], 0, 0, 0);
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sk + mb * 32 * T::kRowBytesK + ka[kk]));
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
     }
-
-  // Keep the K operand reads 4 groups ahead of the MFMAs that consume them
-  // (LDS latency spans several 16-cycle MFMAs).
+  // Keep the K operand reads 4 ahead of the MFMAs that consume them (LDS
+  // latency spans a few MFMAs).
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-  for (int j = 0; j < KB * KK - 4; ++j) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+  for (int j = 0; j < MB * KK - 4; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   if (masked) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 32 * (kb / 2) + 8 * h + 4 * (kb % 2) + i >= key_end) s[kb][qb][i] = -INFINITY;
+      for (int r = 0; r < 16; ++r)
+        if (t0 + 32 * mb + 16 * (r / 8) + 8 * h + 4 * ((r / 4) % 2) + r % 4 >= key_end) s[mb][r] = -INFINITY;
   }
-  // Rescale test without the cross-lane max: a query needs a new max only if
-  // one of its raw scores exceeds thr = (m + 2^8 headroom) / scale_log2, and
-  // every lane can test its own 16 scores of each query.  The 4-lane max is
-  // taken only in the rare branch.
-  float lm[2];
+  // Rescale test without the cross-lane max: the query needs a new max only
+  // if one of its raw scores exceeds thr = (m + 2^8 headroom) / scale_log2,
+  // and each lane can test its own 32 scores.  The 2-lane max is taken only
+  // in the rare branch.
+  float lm;
+  {
+    float a[MB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float a = max3f(s[0][qb][0], s[0][qb][1], s[0][qb][2]);
-    float b = max3f(s[0][qb][3], s[1][qb][0], s[1][qb][1]);
-    float c = max3f(s[1][qb][2], s[1][qb][3], s[2][qb][0]);
-    float d = max3f(s[2][qb][1], s[2][qb][2], s[2][qb][3]);
-    float e = max3f(s[3][qb][0], s[3][qb][1], s[3][qb][2]);
-    a = max3f(a, b, s[3][qb][3]);
-    c = max3f(c, d, e);
-    lm[qb] = max2f(a, c);
-  }
-  if (__any(lm[0] > thr[0] || lm[1] > thr[1])) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m_new = fmaxf(m[qb], quad_max(lm[qb]) * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
-      lsum[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
-      m[qb] = m_new;
-      thr[qb] = (m_new + kRescaleLog2) / scale_log2;
+    for (int mb = 0; mb < MB; ++mb) {
+      float b0 = max3f(s[mb][0], s[mb][1], s[mb][2]);
+      float b1 = max3f(s[mb][3], s[mb][4], s[mb][5]);
+      float b2 = max3f(s[mb][6], s[mb][7], s[mb][8]);
+      float b3 = max3f(s[mb][9], s[mb][10], s[mb][11]);
+      float b4 = max3f(s[mb][12], s[mb][13], s[mb][14]);
+      b0 = max3f(b0, b1, s[mb][15]);
+      b2 = max3f(b2, b3, b4);
+      a[mb] = max2f(b0, b2);
     }
+    lm = a[0];
+#pragma unroll
+    for (int mb = 1; mb < MB; ++mb) lm = max2f(lm, a[mb]);
+  }
+  if (__any(lm > thr)) {
+    const float m_new = fmaxf(m, pair_max(lm) * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    m = m_new;
+    thr = (m_new + kRescaleLog2) / scale_log2;
   }
 
   const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x8 pf[KS][2];
+  bf16x8 pf[KS];
+  const float neg_m = -m;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float neg_m = -m[qb];
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], scale_log2, neg_m));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i + 1], scale_log2, neg_m));
-        const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-        lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, lsum[qb], false);
-        pf[kb / 2][qb][4 * (kb % 2) + i] = pk[0];
-        pf[kb / 2][qb][4 * (kb % 2) + i + 1] = pk[1];
-      }
-  }
+    for (int r = 0; r < 16; r += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], scale_log2, neg_m));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r + 1], scale_log2, neg_m));
+      const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, lsum, false);
+      pf[2 * mb + r / 8][r % 8] = pk[0];
+      pf[2 * mb + r / 8][r % 8 + 1] = pk[1];
+    }
 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sv + db * 16 * T::kRowBytesV + va[ks]));
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[ks][qb], o[db][qb], 0, 0, 0);
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sv + db * 32 * T::kRowBytesV + va[ks]));
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
     }
   // same read-ahead for the V^T operands
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
   for (int j = 0; j < KS * DB - 4; ++j) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
   using T = Tile<D>;
-  constexpr int KK = D / 32;
-  constexpr int DB = D / 16;
+  constexpr int KK = D / 16;
+  constexpr int DB = D / 32;
   __shared__ __attribute__((aligned(1024))) char sk0[T::kBytesK], sk1[T::kBytesK];
   __shared__ __attribute__((aligned(1024))) char sv0[T::kBytesV], sv1[T::kBytesV];
 
@@ -433,12 +438,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
 
   // wave index as a scalar: block choices and LDS-DMA bases depend on it
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
-  const int h = lane / 16, c16 = lane % 16;
+  const int h = lane / 32, c32 = lane % 32;
   int ka[KK], va[KS];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) ka[kk] = c16 * T::kRowBytesK + 16 * ((4 * kk + h) ^ swz<T::kChunksK>(c16));
+  for (int kk = 0; kk < KK; ++kk) ka[kk] = c32 * T::kRowBytesK + 16 * ((2 * kk + h) ^ swz<T::kChunksK>(c32));
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) va[ks] = c16 * T::kRowBytesV + 16 * ((4 * ks + h) ^ swz<8>(c16));
+  for (int ks = 0; ks < KS; ++ks) va[ks] = c32 * T::kRowBytesV + 16 * ((2 * ks + h) ^ swz<8>(c32));
 
   LaneSlots<D> slots;
 #pragma unroll
@@ -449,26 +454,25 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
   RunCursor cursor;
   cursor_seek<D>(runs, cursor, slots, wave, lane, key_begin);
 
-  // Q^T B operand: lane holds head dims 32kk + 8h .. +8 of query 16qb + c16.
-  bf16x8 qf[KK][2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q_row = qt * QT + wave * 32 + 16 * qb + c16;
-    const bool ok = q_row < p.n_queries;
-    const uint16_t* qp = p.q + ((long long)(ok ? q_row : 0) * p.num_heads + head) * D + 8 * h;
+  // Q^T B operand: lane holds head dims 16kk + 8h .. +8 of query c32.
+  const int q_row = qt * QT + wave * 32 + c32;
+  const bool q_ok = q_row < p.n_queries;
+  bf16x8 qf[KK];
+  {
+    const uint16_t* qp = p.q + ((long long)(q_ok ? q_row : 0) * p.num_heads + head) * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[kk][qb] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0));
+      qf[kk] = as_bf16x8(q_ok ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0));
   }
 
-  f32x4 o[DB][2];
+  f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};  // running max of scaled scores (log2 domain), per query block
-  float lsum[2] = {0.f, 0.f};  // this lane's share of the running sums
-  float thr[2] = {-INFINITY, -INFINITY};  // raw-score level that forces a rescale
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = -INFINITY;    // running max of scaled scores (log2 domain)
+  float lsum = 0.f;       // this lane's share of the running sum
+  float thr = -INFINITY;  // raw-score level that forces a rescale
 
   fetch_tile<D>(runs, slots, cursor, wave, lane, t_begin * KT, key_begin, key_end, sk0, sv0);
   for (int t = t_begin; t < t_end; t += 2) {
@@ -481,40 +485,35 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 2 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 2) * KT, key_begin, key_end, sk0, sv0);
-    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, thr, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT, key_end,
-                   h);
+    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, thr, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT,
+                   key_end, h);
   }
 
+  const float ltot = pair_sum(lsum);
+  const float inv = 1.f / ltot;
+  if (!q_ok) return;
+  // lane holds dims 32db + 8g + 4h + (0..3) for g = 0..3
+  if (p.n_splits == 1) {
+    uint16_t* op = p.out + ((long long)q_row * p.num_heads + head) * D + 4 * h;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q_row = qt * QT + wave * 32 + 16 * qb + c16;
-    float ltot = lsum[qb];
-    {
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ltot), __float_as_uint(ltot), false, false);
-      ltot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-      const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(ltot), __float_as_uint(ltot), false, false);
-      ltot = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-    }
-    const float inv = 1.f / ltot;
-    if (q_row >= p.n_queries) continue;
-    if (p.n_splits == 1) {
-      uint16_t* op = p.out + ((long long)q_row * p.num_heads + head) * D + 4 * h;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x2 lo = {(__bf16)(o[db][qb][0] * inv), (__bf16)(o[db][qb][1] * inv)};
-        const bf16x2 hi = {(__bf16)(o[db][qb][2] * inv), (__bf16)(o[db][qb][3] * inv)};
-        *reinterpret_cast<uint2*>(op + 16 * db) =
+      for (int g = 0; g < 4; ++g) {
+        const bf16x2 lo = {(__bf16)(o[db][4 * g] * inv), (__bf16)(o[db][4 * g + 1] * inv)};
+        const bf16x2 hi = {(__bf16)(o[db][4 * g + 2] * inv), (__bf16)(o[db][4 * g + 3] * inv)};
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * g) =
             make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
-    } else {
-      const long long row = ((long long)split * p.n_queries + q_row) * p.num_heads + head;
-      float* op = p.part_o + row * D + 4 * h;
+  } else {
+    const long long row = ((long long)split * p.n_queries + q_row) * p.num_heads + head;
+    float* op = p.part_o + row * D + 4 * h;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<float4*>(op + 16 * db) =
-            make_float4(o[db][qb][0] * inv, o[db][qb][1] * inv, o[db][qb][2] * inv, o[db][qb][3] * inv);
-      if (h == 0) p.part_lse[row] = m[qb] + __log2f(ltot);
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * g) =
+            make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+    if (h == 0) p.part_lse[row] = m + __log2f(ltot);
   }
 }
 
@@ -526,31 +525,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= rows) return;
   const int c4 = threadIdx.x % TPR;
-  // every split's log-sum-exp and values are loaded up front, so a thread has
-  // all its loads in flight at once
-  float lse[kAttnMaxSplits];
-  float4 v[kAttnMaxSplits];
-#pragma unroll
-  for (int j = 0; j < kAttnMaxSplits; ++j) {
-    const bool on = j < p.n_splits;
-    lse[j] = on ? p.part_lse[j * rows + row] : -INFINITY;
-    v[j] = on ? *reinterpret_cast<const float4*>(p.part_o + (j * rows + row) * D + 4 * c4)
-              : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  float mx = lse[0];
-#pragma unroll
-  for (int j = 1; j < kAttnMaxSplits; ++j) mx = fmaxf(mx, lse[j]);
+  float mx = -INFINITY;
+  for (int j = 0; j < p.n_splits; ++j) mx = fmaxf(mx, p.part_lse[j * rows + row]);
   float wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // four splits' values in flight at a time
+  for (int j0 = 0; j0 < p.n_splits; j0 += 4) {
+    float w[4];
+    float4 v[4];
 #pragma unroll
-  for (int j = 0; j < kAttnMaxSplits; ++j) {
-    if (j >= p.n_splits) break;
-    const float w = __builtin_amdgcn_exp2f(lse[j] - mx);
-    wsum += w;
-    acc.x += w * v[j].x;
-    acc.y += w * v[j].y;
-    acc.z += w * v[j].z;
-    acc.w += w * v[j].w;
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i;
+      const bool on = j < p.n_splits;
+      w[i] = on ? __builtin_amdgcn_exp2f(p.part_lse[j * rows + row] - mx) : 0.f;
+      v[i] = on ? *reinterpret_cast<const float4*>(p.part_o + (j * rows + row) * D + 4 * c4)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wsum += w[i];
+      acc.x += w[i] * v[i].x;
+      acc.y += w[i] * v[i].y;
+      acc.z += w[i] * v[i].z;
+      acc.w += w[i] * v[i].w;
+    }
   }
   const float inv = 1.f / wsum;
   const bf16x2 lo = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv)};

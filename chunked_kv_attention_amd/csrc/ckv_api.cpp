@@ -37,7 +37,7 @@ struct Layout {
   size_t tables_off = 0, tables_bytes = 0;
   size_t sink_off = 0, sink_layer_bytes = 0;
   size_t ring_off = 0, ring_bytes = 0;  // per (layer, step)
-  size_t part_o_off = 0, part_lse_off = 0, scratch_queries = 0;
+  size_t part_o_off = 0, part_lse_off = 0;
   size_t text_off = 0, text_layer_bytes = 0;  // per layer: context K [H][max][d], V^T [H][d][max]
   size_t total = 0;
 };
@@ -80,11 +80,10 @@ Layout layout_of(const ckv_config* c) {
   L.ring_off = off;
   L.ring_bytes = align_up(2 * H * (size_t)L.ring_rows * d * sizeof(bf16_t));
   off += L.ring_bytes * c->num_layers * c->num_steps;
-  L.scratch_queries = L.n0 > L.n1 ? L.n0 : L.n1;
   L.part_o_off = off;
-  off = align_up(off + sizeof(float) * kMaxSplits * L.scratch_queries * H * d);
+  off = align_up(off + sizeof(float) * ckv::kAttnScratchRows * d);
   L.part_lse_off = off;
-  off = align_up(off + sizeof(float) * kMaxSplits * L.scratch_queries * H);
+  off = align_up(off + sizeof(float) * ckv::kAttnScratchRows);
   L.text_off = off;
   L.text_layer_bytes = align_up(2 * H * (size_t)CKV_MAX_TEXT_TOKENS * d * sizeof(bf16_t));
   off += L.text_layer_bytes * c->num_layers;
@@ -178,6 +177,9 @@ int splits_for(int num_cus, int heads, int n_queries, int n_keys) {
   // partials cost more than the idle CUs of an unsplit call (measured: an
   // 880 x 512 cross-attention takes 16 us unsplit, 26 us split in two)
   if (p > key_tiles / 8) p = key_tiles / 8;
+  // the partials of every split must fit the scratch rows
+  const long long rows = (long long)n_queries * heads;
+  if (p * rows > ckv::kAttnScratchRows) p = ckv::kAttnScratchRows / rows;
   return p < 1 ? 1 : (int)p;
 }
 
@@ -388,7 +390,6 @@ ckv_status ckv_chunk_attention(ckv_cache* c, int32_t layer, int32_t step, int32_
   p.scale_log2 = c->scale() * 1.4426950408889634f;
   p.part_o = (float*)(c->arena + c->L.part_o_off);
   p.part_lse = (float*)(c->arena + c->L.part_lse_off);
-  if ((size_t)p.n_queries > c->L.scratch_queries) return CKV_E_INVALID;
   return ckv::launch_chunk_attention(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
 }
 

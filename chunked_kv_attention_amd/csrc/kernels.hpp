@@ -72,7 +72,7 @@ struct AttnParams {
   int q_tiles;               // ceil(nq / query tile)
   int key_tiles;             // ceil(n_keys / key tile)
   float scale_log2;          // softmax scale * log2(e)
-  float* part_o;             // [n_splits][nq][H][d] fp32 (split > 1)
+  float* part_o;             // [n_splits][nq][H][d] fp32 (split > 1); n_splits*nq*H <= kAttnScratchRows
   float* part_lse;           // [n_splits][nq][H]   log2-domain LSE (split > 1)
 };
 
@@ -121,7 +121,12 @@ constexpr int kConvChannelTile = 128;  // output channels per workgroup
 
 constexpr int kAttnQueryTile = 128;  // query rows per workgroup
 constexpr int kAttnKeyTile = 64;     // keys per LDS tile
-constexpr int kAttnMaxSplits = 4;    // most key splits of one call (partial-area size)
+constexpr int kAttnMaxSplits = 32;   // most key splits of one call
+// Rows (query, head) of float32 partials the split scratch holds: every split
+// workgroup of a call owns one query tile of one head, and a call is split
+// only while its workgroups fit the chip's 2-per-CU slots once, so 2 x 256
+// CUs x 128 rows bound every split call on MI355X.
+constexpr int kAttnScratchRows = 2 * 256 * kAttnQueryTile;
 
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s);
 hipError_t launch_rope_table(const RopeTableParams& p, hipStream_t s);

@@ -289,18 +289,20 @@ def test_single_chunk_880x19360_peaky():
     assert splits > 1  # the split-key path and its merge are exercised
 
 
-def test_four_key_splits_three_heads_880x19360():
+def test_many_key_splits_three_heads_880x19360():
     """One GPU's share of 24 heads sharded 8 ways ("Learning Video Generation
     from the Wan2.2 Source Code", Ch.8, Ulysses: split heads, not the
     sequence): 3 heads x 880 queries x 19,360 keys, which fills the chip only
-    with 4 key splits.  Chunk 19 (peaky) and chunk 20 (its ring window wraps
-    into two runs), sampled rows."""
+    with many key splits (24: 21 query tiles x 24 = 504 workgroups).  Chunk
+    19 (peaky) and chunk 20 (its ring window wraps into two runs), sampled
+    rows."""
     cfg = C.Config(1, 1, 3, 128, 22, 40, 3, 18, 29)
     r = G.Rollout(cfg, base_seed=13, rows_per_call=128, f64_bar=False)
-    assert r.cache.attention_splits(880, 19360) == 4
+    splits = r.cache.attention_splits(880, 19360)
+    assert splits > 4, splits
     mx, rl2 = _peaky_window_up_to_chunk_19(r, 13)
     mx20, rl20 = r.step("chunk", 0, 0, 20)
-    print(f"3 heads x 880 x 19360, 4 splits: chunk 19 max abs {mx:.3e} rel L2 {rl2:.3e}; chunk 20 max abs "
+    print(f"3 heads x 880 x 19360, {splits} splits: chunk 19 max abs {mx:.3e} rel L2 {rl2:.3e}; chunk 20 max abs "
           f"{mx20:.3e} rel L2 {rl20:.3e}; unrounded float64 q/k worst {r.worst64[0]:.3e} / {r.worst64[1]:.3e} "
           f"(oracles differ by {r.worst_pair[0]:.3e} / {r.worst_pair[1]:.3e})")
 
