@@ -122,25 +122,12 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// max of finite floats without the quieting of NaN inputs that fmaxf implies
-__device__ inline float max3f(float a, float b, float c) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-#else
-  return fmaxf(a, fmaxf(b, c));
-#endif
-}
-__device__ inline float max2f(float a, float b) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-#else
-  return fmaxf(a, b);
-#endif
-}
+// Max of two / three floats, as compiler builtins: the scores they read come
+// straight from MFMA accumulators, and only instructions the compiler can see
+// get the wait states a VALU read of an MFMA result needs (an inline-asm max
+// here read accumulators that were still being written).
+__device__ inline float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+__device__ inline float max2f(float a, float b) { return __builtin_fmaxf(a, b); }
 
 // The up to three runs of this head's window, loaded once into uniform
 // scalars (no indexed access to the parameter block, which would force a

@@ -382,3 +382,31 @@ def test_errors_do_not_launch():
     assert e.value.status == C.CKV_E_STATE
     with pytest.raises(ValueError):
         cache.chunk_attention(0, 0, 0, x, x)  # wrong shape for chunk 0
+
+
+def test_repeated_calls_are_bit_identical():
+    """The same call on the same cache gives the same bits every time (the
+    kernels have no order-dependent reductions): chunk 19 of the profile at
+    head_dim 128 (3 key splits + merge) and the 2640-token sink pass (one
+    split), four calls each."""
+    cfg = C.Config(1, 1, 24, 128, 22, 40, 3, 18, 29)
+    cache = C.Cache(cfg)
+    H, d = cfg.num_heads, cfg.head_dim
+    qs = {}
+    for c in range(0, 20):
+        q, k, v = (G.to_dev(b) for b in I.draw_qkv_bits(cfg.tokens(c), H, d, base_seed=41, chunk=c,
+                                                          step_code=1 if c == 0 else 0))
+        qs[c] = torch.empty_like(q)
+        if c == 0:
+            cache.sink_build(0, q, k, v, qs[c])
+        else:
+            cache.rope_append(0, 0, c, q, k, v, qs[c])
+    for step, chunk in ((0, 19), (C.STEP_SINK, 0)):
+        outs = []
+        for _ in range(4):
+            o = torch.empty_like(qs[chunk])
+            cache.chunk_attention(0, step, chunk, qs[chunk], o)
+            torch.cuda.synchronize()
+            outs.append(G.bits_of(o))
+        for other in outs[1:]:
+            np.testing.assert_array_equal(other, outs[0])
