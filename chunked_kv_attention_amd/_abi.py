@@ -24,7 +24,8 @@ CONV_CACHE_T = 2
 EXPORTS = (
     "ckv_cache_bytes", "ckv_cache_create", "ckv_cache_create_dry", "ckv_cache_reset",
     "ckv_cache_destroy", "ckv_rope_append", "ckv_sink_build", "ckv_norm_rope_append",
-    "ckv_norm_sink_build", "ckv_chunk_attention", "ckv_text_store", "ckv_cross_attention",
+    "ckv_norm_sink_build", "ckv_chunk_attention", "ckv_chunk_attention_static", "ckv_text_store",
+    "ckv_cross_attention",
     "ckv_window", "ckv_ring_slot", "ckv_debug_copy_kv", "ckv_attention_splits",
     "ckv_status_string",
     "ckv_conv_bytes", "ckv_conv_create", "ckv_conv_create_dry", "ckv_conv_set_weights", "ckv_conv_reset",
@@ -92,6 +93,7 @@ def load() -> ctypes.CDLL:
         "ckv_norm_rope_append": (I32, [P, I32, I32, I32, P, P, P, P, P, ctypes.c_float, P, P]),
         "ckv_norm_sink_build": (I32, [P, I32, P, P, P, P, P, ctypes.c_float, P, P]),
         "ckv_chunk_attention": (I32, [P, I32, I32, I32, P, P, P]),
+        "ckv_chunk_attention_static": (I32, [P, I32, I32, I32, P, P, P]),
         "ckv_text_store": (I32, [P, I32, P, P, I32, P]),
         "ckv_cross_attention": (I32, [P, I32, I32, P, P, P]),
         "ckv_window": (I32, [P, I32, I32, I32, ctypes.POINTER(CkvSegment), I32, ctypes.POINTER(I32)]),
@@ -248,6 +250,14 @@ class Cache:
         _check(self._lib.ckv_chunk_attention(self._h, layer, step, chunk, self._ptr(q_rot, sh, "q_rot"),
                                              self._ptr(out, sh, "out"), self._stream(stream)),
                "ckv_chunk_attention")
+
+    def chunk_attention_static(self, layer, step, chunk, q_rot, out, stream=None):
+        """ckv_chunk_attention_static: the same call with the split partials in
+        the library's own static device array (allocates nothing)."""
+        sh = self._shape(chunk)
+        _check(self._lib.ckv_chunk_attention_static(self._h, layer, step, chunk, self._ptr(q_rot, sh, "q_rot"),
+                                                    self._ptr(out, sh, "out"), self._stream(stream)),
+               "ckv_chunk_attention_static")
 
     def text_store(self, layer, k_text, v_text, stream=None):
         """Store the layer's context: k_text, v_text [n_text][H][d] bf16 device tensors."""

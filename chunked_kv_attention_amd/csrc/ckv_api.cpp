@@ -265,6 +265,72 @@ ckv_status sink_impl(ckv_cache* c, int32_t layer, const void* q, const void* k, 
   return CKV_OK;
 }
 
+ckv_status attention_impl(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk, const void* q_rot, void* out,
+                          void* stream, bool static_scratch) {
+  if (!c) return CKV_E_INVALID;
+  if (!ptr_ok(q_rot) || !ptr_ok(out)) return CKV_E_INVALID;
+  ckv_status st = to_status(c->sched.check_attention(layer, step, chunk));
+  if (st != CKV_OK) return st;
+  if (c->dry) return CKV_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = ensure_device(c, s)) != CKV_OK) return st;
+
+  ckv::Segment segs[3];
+  const int nseg = c->sched.window(chunk, segs);
+  const long long d = c->cfg.head_dim;
+  ckv::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  int end = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (i < nseg) {
+      const ckv::Segment& g = segs[i];
+      if (g.kind == 0) {
+        p.k[i] = c->sink_k(layer);
+        p.vt[i] = c->sink_vt(layer);
+        p.k_head_stride[i] = (long long)c->L.n0 * d;
+        p.vt_head_stride[i] = d * c->L.n0;
+        p.vt_row_stride[i] = c->L.n0;
+      } else {
+        p.k[i] = c->ring_k(layer, step) + (size_t)g.first_slot * c->L.n1 * d;
+        p.vt[i] = c->ring_vt(layer, step) + (size_t)g.first_slot * c->L.n1;
+        p.k_head_stride[i] = (long long)c->L.ring_rows * d;
+        p.vt_head_stride[i] = d * c->L.ring_rows;
+        p.vt_row_stride[i] = c->L.ring_rows;
+      }
+      end += g.n_tokens;
+    } else {
+      p.k[i] = p.k[0];
+      p.vt[i] = p.vt[0];
+      p.k_head_stride[i] = p.k_head_stride[0];
+      p.vt_head_stride[i] = p.vt_head_stride[0];
+      p.vt_row_stride[i] = p.vt_row_stride[0];
+    }
+    p.seg_end[i] = end;
+  }
+  p.q = (const bf16_t*)q_rot;
+  p.out = (bf16_t*)out;
+  p.n_queries = c->tokens(chunk);
+  p.n_keys = end;
+  p.num_heads = c->cfg.num_heads;
+  p.n_splits = splits_for(c->num_cus, c->cfg.num_heads, p.n_queries, p.n_keys);
+  p.q_tiles = (p.n_queries + ckv::kAttnQueryTile - 1) / ckv::kAttnQueryTile;
+  p.key_tiles = (p.n_keys + ckv::kAttnKeyTile - 1) / ckv::kAttnKeyTile;
+  p.scale_log2 = c->scale() * 1.4426950408889634f;
+  if (static_scratch) {
+    // the library's own array: partial outputs, then the log-sum-exps
+    const size_t rows = (size_t)p.n_splits * p.n_queries * p.num_heads;
+    if (p.n_splits > 1 && rows * (d + 1) * sizeof(float) > ckv::kStaticScratchBytes) return CKV_E_INVALID;
+    void* base = nullptr;
+    if (ckv::static_scratch(&base) != hipSuccess) return CKV_E_HIP;
+    p.part_o = (float*)base;
+    p.part_lse = (float*)base + rows * d;
+  } else {
+    p.part_o = (float*)(c->arena + c->L.part_o_off);
+    p.part_lse = (float*)(c->arena + c->L.part_lse_off);
+  }
+  return ckv::launch_chunk_attention(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -339,58 +405,12 @@ ckv_status ckv_norm_sink_build(ckv_cache* c, int32_t layer, const void* q, const
 
 ckv_status ckv_chunk_attention(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk, const void* q_rot,
                                void* out, void* stream) {
-  if (!c) return CKV_E_INVALID;
-  if (!ptr_ok(q_rot) || !ptr_ok(out)) return CKV_E_INVALID;
-  ckv_status st = to_status(c->sched.check_attention(layer, step, chunk));
-  if (st != CKV_OK) return st;
-  if (c->dry) return CKV_OK;
-  hipStream_t s = (hipStream_t)stream;
-  if ((st = ensure_device(c, s)) != CKV_OK) return st;
+  return attention_impl(c, layer, step, chunk, q_rot, out, stream, false);
+}
 
-  ckv::Segment segs[3];
-  const int nseg = c->sched.window(chunk, segs);
-  const long long d = c->cfg.head_dim;
-  ckv::AttnParams p;
-  std::memset(&p, 0, sizeof(p));
-  int end = 0;
-  for (int i = 0; i < 3; ++i) {
-    if (i < nseg) {
-      const ckv::Segment& g = segs[i];
-      if (g.kind == 0) {
-        p.k[i] = c->sink_k(layer);
-        p.vt[i] = c->sink_vt(layer);
-        p.k_head_stride[i] = (long long)c->L.n0 * d;
-        p.vt_head_stride[i] = d * c->L.n0;
-        p.vt_row_stride[i] = c->L.n0;
-      } else {
-        p.k[i] = c->ring_k(layer, step) + (size_t)g.first_slot * c->L.n1 * d;
-        p.vt[i] = c->ring_vt(layer, step) + (size_t)g.first_slot * c->L.n1;
-        p.k_head_stride[i] = (long long)c->L.ring_rows * d;
-        p.vt_head_stride[i] = d * c->L.ring_rows;
-        p.vt_row_stride[i] = c->L.ring_rows;
-      }
-      end += g.n_tokens;
-    } else {
-      p.k[i] = p.k[0];
-      p.vt[i] = p.vt[0];
-      p.k_head_stride[i] = p.k_head_stride[0];
-      p.vt_head_stride[i] = p.vt_head_stride[0];
-      p.vt_row_stride[i] = p.vt_row_stride[0];
-    }
-    p.seg_end[i] = end;
-  }
-  p.q = (const bf16_t*)q_rot;
-  p.out = (bf16_t*)out;
-  p.n_queries = c->tokens(chunk);
-  p.n_keys = end;
-  p.num_heads = c->cfg.num_heads;
-  p.n_splits = splits_for(c->num_cus, c->cfg.num_heads, p.n_queries, p.n_keys);
-  p.q_tiles = (p.n_queries + ckv::kAttnQueryTile - 1) / ckv::kAttnQueryTile;
-  p.key_tiles = (p.n_keys + ckv::kAttnKeyTile - 1) / ckv::kAttnKeyTile;
-  p.scale_log2 = c->scale() * 1.4426950408889634f;
-  p.part_o = (float*)(c->arena + c->L.part_o_off);
-  p.part_lse = (float*)(c->arena + c->L.part_lse_off);
-  return ckv::launch_chunk_attention(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
+ckv_status ckv_chunk_attention_static(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk, const void* q_rot,
+                                      void* out, void* stream) {
+  return attention_impl(c, layer, step, chunk, q_rot, out, stream, true);
 }
 
 ckv_status ckv_text_store(ckv_cache* c, int32_t layer, const void* k_text, const void* v_text, int32_t n_text,

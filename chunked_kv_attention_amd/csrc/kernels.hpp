@@ -128,6 +128,12 @@ constexpr int kAttnMaxSplits = 32;   // most key splits of one call
 // CUs x 128 rows bound every split call on MI355X.
 constexpr int kAttnScratchRows = 2 * 256 * kAttnQueryTile;
 
+// Bytes of the library's static split scratch (float32 partial outputs at
+// head_dim 128 plus log-sum-exps for every scratch row), and its device
+// address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)kAttnScratchRows * (128 + 1) * sizeof(float);
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s);
 hipError_t launch_rope_table(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_text_store(const TextStoreParams& p, int head_dim, hipStream_t s);

@@ -258,3 +258,36 @@ def test_cache_bytes_include_one_context_per_layer():
     rings = 4 * 2 * 24 * 19 * 880 * 128 * 2
     text = 2 * 24 * 512 * 128 * 2
     assert more - one == sink + rings + text
+
+
+def test_static_scratch_entry_point_follows_the_same_checks():
+    """ckv_chunk_attention_static validates and orders exactly like
+    ckv_chunk_attention (dry cache: no device work)."""
+    lib = C.load()
+    cfg = TINY.to_c()
+    h = ctypes.c_void_p()
+    assert lib.ckv_cache_create_dry(ctypes.byref(cfg), ctypes.byref(h)) == C.CKV_OK
+    try:
+        for fn in (lib.ckv_chunk_attention, lib.ckv_chunk_attention_static):
+            assert fn(h, 0, 0, 1, FAKE, FAKE, None) == C.CKV_E_STATE      # no sink yet
+            assert fn(None, 0, 0, 1, FAKE, FAKE, None) == C.CKV_E_INVALID
+            assert fn(h, 0, 0, 1, FAKE + 8, FAKE, None) == C.CKV_E_INVALID  # misaligned
+        assert lib.ckv_sink_build(h, 0, FAKE, FAKE, FAKE, FAKE, None) == C.CKV_OK
+        assert lib.ckv_rope_append(h, 0, 0, 1, FAKE, FAKE, FAKE, FAKE, None) == C.CKV_OK
+        for fn in (lib.ckv_chunk_attention, lib.ckv_chunk_attention_static):
+            assert fn(h, 0, 0, 1, FAKE, FAKE, None) == C.CKV_OK
+            assert fn(h, 0, 0, 2, FAKE, FAKE, None) == C.CKV_E_ORDER       # chunk 2 not appended
+            assert fn(h, 0, C.STEP_SINK, 0, FAKE, FAKE, None) == C.CKV_OK
+    finally:
+        lib.ckv_cache_destroy(h)
+
+
+def test_static_scratch_size_in_header_covers_every_split_call():
+    """The header's CKV_STATIC_SCRATCH_BYTES holds the float32 partials and
+    log-sum-exps of the largest split call the split policy allows (2 slots x
+    256 CUs x 128 query rows, head_dim 128)."""
+    header = open(os.path.join(ROOT, "include", "ckv.h")).read()
+    m = re.search(r"#define CKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) \* (\d+) \* (\d+) \* \((\d+) \+ 1\) \* 4\)", header)
+    assert m, "define not found"
+    slots, cus, rows, d = (int(x) for x in m.groups())
+    assert slots * cus * rows * (d + 1) * 4 == 2 * 256 * 128 * 129 * 4
