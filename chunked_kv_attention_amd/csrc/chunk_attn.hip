@@ -45,8 +45,9 @@
 //
 // Occupancy.  880 queries x 24 heads is only 168 workgroups of 128 rows for
 // 256 CUs (21 for a 3-head share), so the key range is split into as many
-// parts as fill the chip's workgroup slots once (3 and 24 parts there); each part writes normalised fp32 partials and a log2-domain
-// log-sum-exp, and a second kernel merges them (softmax over a concatenation
+// parts as fill the chip's workgroup slots once (3 and 24 parts there); each
+// part writes normalised fp16 partials and a float32 log2-domain log-sum-exp,
+// and a second kernel merges them in float32 (softmax over a concatenation
 // equals the LSE-weighted merge of per-part softmaxes).
 //
 // L2 locality.  Workgroups are dispatched round-robin over the 8 XCDs, each
@@ -64,6 +65,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int QT = kAttnQueryTile;  // 128
@@ -493,13 +495,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
       }
   } else {
     const long long row = ((long long)split * p.n_queries + q_row) * p.num_heads + head;
-    float* op = p.part_o + row * D + 4 * h;
+    uint16_t* op = p.part_o + row * D + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(op + 32 * db + 8 * g) =
-            make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      for (int g = 0; g < 4; ++g) {
+        // normalised partials (|o| <= max |v|) in fp16: 11 significant bits
+        const half2 lo = {(_Float16)(o[db][4 * g] * inv), (_Float16)(o[db][4 * g + 1] * inv)};
+        const half2 hi = {(_Float16)(o[db][4 * g + 2] * inv), (_Float16)(o[db][4 * g + 3] * inv)};
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * g) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      }
     if (h == 0) p.part_lse[row] = m + __log2f(ltot);
   }
 }
@@ -525,8 +531,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
       const int j = j0 + i;
       const bool on = j < p.n_splits;
       w[i] = on ? __builtin_amdgcn_exp2f(p.part_lse[j * rows + row] - mx) : 0.f;
-      v[i] = on ? *reinterpret_cast<const float4*>(p.part_o + (j * rows + row) * D + 4 * c4)
-                : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (on) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p.part_o + (j * rows + row) * D + 4 * c4);
+        const half2 lo = __builtin_bit_cast(half2, u.x), hi = __builtin_bit_cast(half2, u.y);
+        v[i] = make_float4((float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]);
+      } else {
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

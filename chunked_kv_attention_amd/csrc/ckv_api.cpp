@@ -81,7 +81,7 @@ Layout layout_of(const ckv_config* c) {
   L.ring_bytes = align_up(2 * H * (size_t)L.ring_rows * d * sizeof(bf16_t));
   off += L.ring_bytes * c->num_layers * c->num_steps;
   L.part_o_off = off;
-  off = align_up(off + sizeof(float) * ckv::kAttnScratchRows * d);
+  off = align_up(off + sizeof(uint16_t) * ckv::kAttnScratchRows * d);
   L.part_lse_off = off;
   off = align_up(off + sizeof(float) * ckv::kAttnScratchRows);
   L.text_off = off;
@@ -319,13 +319,14 @@ ckv_status attention_impl(ckv_cache* c, int32_t layer, int32_t step, int32_t chu
   if (static_scratch) {
     // the library's own array: partial outputs, then the log-sum-exps
     const size_t rows = (size_t)p.n_splits * p.n_queries * p.num_heads;
-    if (p.n_splits > 1 && rows * (d + 1) * sizeof(float) > ckv::kStaticScratchBytes) return CKV_E_INVALID;
+    if (p.n_splits > 1 && rows * (d * sizeof(uint16_t) + sizeof(float)) > ckv::kStaticScratchBytes)
+      return CKV_E_INVALID;
     void* base = nullptr;
     if (ckv::static_scratch(&base) != hipSuccess) return CKV_E_HIP;
-    p.part_o = (float*)base;
-    p.part_lse = (float*)base + rows * d;
+    p.part_o = (uint16_t*)base;
+    p.part_lse = (float*)((char*)base + rows * d * sizeof(uint16_t));
   } else {
-    p.part_o = (float*)(c->arena + c->L.part_o_off);
+    p.part_o = (uint16_t*)(c->arena + c->L.part_o_off);
     p.part_lse = (float*)(c->arena + c->L.part_lse_off);
   }
   return ckv::launch_chunk_attention(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
@@ -466,7 +467,7 @@ ckv_status ckv_cross_attention(ckv_cache* c, int32_t layer, int32_t chunk, const
   p.q_tiles = (p.n_queries + ckv::kAttnQueryTile - 1) / ckv::kAttnQueryTile;
   p.key_tiles = (p.n_keys + ckv::kAttnKeyTile - 1) / ckv::kAttnKeyTile;
   p.scale_log2 = c->scale() * 1.4426950408889634f;
-  p.part_o = (float*)(c->arena + c->L.part_o_off);
+  p.part_o = (uint16_t*)(c->arena + c->L.part_o_off);
   p.part_lse = (float*)(c->arena + c->L.part_lse_off);
   return ckv::launch_chunk_attention(p, c->cfg.head_dim, s) == hipSuccess ? CKV_OK : CKV_E_HIP;
 }

@@ -72,7 +72,7 @@ struct AttnParams {
   int q_tiles;               // ceil(nq / query tile)
   int key_tiles;             // ceil(n_keys / key tile)
   float scale_log2;          // softmax scale * log2(e)
-  float* part_o;             // [n_splits][nq][H][d] fp32 (split > 1); n_splits*nq*H <= kAttnScratchRows
+  uint16_t* part_o;          // [n_splits][nq][H][d] fp16 (split > 1); n_splits*nq*H <= kAttnScratchRows
   float* part_lse;           // [n_splits][nq][H]   log2-domain LSE (split > 1)
 };
 
@@ -128,10 +128,10 @@ constexpr int kAttnMaxSplits = 32;   // most key splits of one call
 // CUs x 128 rows bound every split call on MI355X.
 constexpr int kAttnScratchRows = 2 * 256 * kAttnQueryTile;
 
-// Bytes of the library's static split scratch (float32 partial outputs at
-// head_dim 128 plus log-sum-exps for every scratch row), and its device
-// address on the current device (looked up once per device).
-constexpr size_t kStaticScratchBytes = (size_t)kAttnScratchRows * (128 + 1) * sizeof(float);
+// Bytes of the library's static split scratch (fp16 partial outputs at
+// head_dim 128 plus float32 log-sum-exps for every scratch row), and its
+// device address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)kAttnScratchRows * (128 * 2 + 4);
 hipError_t static_scratch(void** ptr);
 
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s);

@@ -111,7 +111,9 @@ __device__ inline float sum_sq8(const uint4& v) {
 constexpr int kGroup = 8;  // 16-byte chunks a lane holds at once (512 per wave)
 
 // Two kinds of workgroup in one launch.
-//  * The first qk_blocks: one wave per token, covering q and k of all heads
+//  * The first qk_blocks rotate q and k.  Without the QK-Norm: one thread per
+//    16-byte chunk (flat over token x chunk).  With it: one wave per token,
+//    covering q and k of all heads
 //    (the token's whole projected vector, H*d values): consecutive lanes take
 //    consecutive 16-byte chunks, so loads and stores are fully coalesced, and
 //    with the QK-Norm the wave holds every value of the token for its mean of
@@ -128,7 +130,31 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeAppendParams 
   const float2* tab_h = tab_t + p.n_frames_table * Pt;
   const float2* tab_w = tab_h + p.grid_h * Ph;
 
-  if ((int)blockIdx.x < qk_blocks) {
+  if (!kNorm && (int)blockIdx.x < qk_blocks) {
+    // Without the norm the rotation is elementwise: one thread per 16-byte
+    // chunk of q and of k (a flat grid over token x chunk, like a copy), the
+    // two loads issued before any table lookup.
+    const int W8 = H * C8;  // chunks per token
+    const long long e = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= (long long)p.n_tokens * W8) return;
+    const int tok = (int)(e / W8);
+    const int c = (int)(e - (long long)tok * W8);
+    const uint4 qv = *reinterpret_cast<const uint4*>(p.q + e * 8);
+    const uint4 kv = *reinterpret_cast<const uint4*>(p.k + e * 8);
+    const int per_frame = p.grid_h * p.grid_w;
+    const int fl = tok / per_frame;
+    const int rem = tok - fl * per_frame;
+    const int row = rem / p.grid_w;
+    const int col = rem - row * p.grid_w;
+    const int head = c / C8, cc = c % C8;
+    uint4 qo, ko;
+    rotate8<D>(qv, qo, cc * 4, p.first_frame + fl, row, col, tab_t, tab_h, tab_w);
+    rotate8<D>(kv, ko, cc * 4, p.first_frame + fl, row, col, tab_t, tab_h, tab_w);
+    *reinterpret_cast<uint4*>(p.q_rot + e * 8) = qo;
+    *reinterpret_cast<uint4*>(p.k_dst + head * p.k_head_stride + (long long)tok * D + cc * 8) = ko;
+    return;
+  }
+  if (kNorm && (int)blockIdx.x < qk_blocks) {
     const int tok = blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
     const int lane = threadIdx.x % 64;
     if (tok >= p.n_tokens) return;  // no barrier on this path
@@ -307,10 +333,13 @@ __global__ __launch_bounds__(256) void copy_kv_kernel(CopyKVParams p) {
 
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s) {
   if (p.n_tokens <= 0 || p.num_heads <= 0) return hipErrorInvalidValue;
-  const int qk_blocks = (p.n_tokens + kThreads / 64 - 1) / (kThreads / 64);
+  const bool norm = p.q_gain != nullptr;
+  // the norm needs a token's whole vector in one wave; the plain rotation is a
+  // flat grid over 16-byte chunks
+  const long long chunks = (long long)p.n_tokens * p.num_heads * (head_dim / 8);
+  const int qk_blocks = norm ? (p.n_tokens + kThreads / 64 - 1) / (kThreads / 64) : (int)((chunks + kThreads - 1) / kThreads);
   const int v_blocks = ((p.n_tokens + kTok - 1) / kTok) * p.num_heads;
   const dim3 grid(qk_blocks + v_blocks);
-  const bool norm = p.q_gain != nullptr;
   if (head_dim == 128 && norm)
     hipLaunchKernelGGL((rope_append_kernel<128, true>), grid, dim3(kThreads), 0, s, p, qk_blocks);
   else if (head_dim == 128)

@@ -188,14 +188,14 @@ ckv_status ckv_chunk_attention(ckv_cache* c, int32_t layer, int32_t step, int32_
 /* The same chunk attention for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): identical arguments, checks, kernels and results, but the
- * float32 partials of a key-split call live in the library's own static
+ * partials (fp16 outputs, float32 log-sum-exps) of a key-split call live in the library's own static
  * device array (CKV_STATIC_SCRATCH_BYTES per GPU, held until the process
  * ends) instead of the cache arena.  Allocates nothing.  Every call on one
  * GPU shares that array: calls that overlap in time on one GPU (two streams,
  * two caches) race, so order them on one stream.  A call whose partials
  * would exceed the array returns CKV_E_INVALID and enqueues nothing (the
  * split policy keeps every call of a valid config within it). */
-#define CKV_STATIC_SCRATCH_BYTES ((size_t)2 * 256 * 128 * (128 + 1) * 4)
+#define CKV_STATIC_SCRATCH_BYTES ((size_t)2 * 256 * 128 * (128 * 2 + 4))
 ckv_status ckv_chunk_attention_static(ckv_cache* c, int32_t layer, int32_t step, int32_t chunk,
                                       const void* q_rot, void* out, void* stream);
 

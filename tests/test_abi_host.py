@@ -283,11 +283,11 @@ def test_static_scratch_entry_point_follows_the_same_checks():
 
 
 def test_static_scratch_size_in_header_covers_every_split_call():
-    """The header's CKV_STATIC_SCRATCH_BYTES holds the float32 partials and
-    log-sum-exps of the largest split call the split policy allows (2 slots x
-    256 CUs x 128 query rows, head_dim 128)."""
+    """The header's CKV_STATIC_SCRATCH_BYTES holds the fp16 partials and
+    float32 log-sum-exps of the largest split call the split policy allows
+    (2 slots x 256 CUs x 128 query rows, head_dim 128)."""
     header = open(os.path.join(ROOT, "include", "ckv.h")).read()
-    m = re.search(r"#define CKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) \* (\d+) \* (\d+) \* \((\d+) \+ 1\) \* 4\)", header)
+    m = re.search(r"#define CKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) \* (\d+) \* (\d+) \* \((\d+) \* 2 \+ 4\)\)", header)
     assert m, "define not found"
     slots, cus, rows, d = (int(x) for x in m.groups())
-    assert slots * cus * rows * (d + 1) * 4 == 2 * 256 * 128 * 129 * 4
+    assert slots * cus * rows * (d * 2 + 4) == 2 * 256 * 128 * (128 * 2 + 4)
