@@ -184,12 +184,18 @@ def summarise_counters(fetch_csv, write_csv):
 
 
 def cpu_baseline(cfg, heads, calls=6):
-    """The float64 oracle, untuned, on a bounded sample of the same workload:
-    the rotation of the sink's and chunks 1..18's keys, then `calls` steady-
-    state chunk steps at step 0 (chunks 19, 20, ...: rotate q/k, record K/V,
-    attend 880 queries x 19,360 keys) for `heads` heads -- the rollout's
-    steady state, about 10 s of host work.  Rate = those attentions'
-    algorithmic FLOPs / wall time (rotations included in the time)."""
+    """The float64 oracle, untuned, on a bounded sample of the same workload
+    (about 12 s of host work):
+      * the rotation of the sink's and chunks 1..18's keys, then `calls`
+        steady-state chunk steps at step 0 (chunks 19, 20, ...: rotate q/k,
+        record K/V, attend 880 queries x 19,360 keys) for `heads` heads;
+      * one first-chunk step (2640 x 2640 self-attention, the bootstrap of
+        the 1280x704 profile), timed on its own.
+    Rate = the steady-state attentions' algorithmic FLOPs / wall time
+    (rotations included).  The whole 1-layer 29-chunk rollout is then
+    extrapolated, not timed: each of its 117 attention calls at the rate
+    measured for its kind (bootstrap rate for chunk 0's 5 calls, steady-state
+    rate for the rest), plus the measured rotation time per call."""
     import numpy as np
 
     import oracle.ckv_oracle as O
@@ -218,6 +224,19 @@ def cpu_baseline(cfg, heads, calls=6):
         assert np.isfinite(out).all()
     dt = time.perf_counter() - t0
     flops = sum(4 * cfg.tokens(c) * keys_of(cfg, c) * heads * cfg.head_dim for c in range(19, last + 1))
+    rate = flops / dt
+    # one bootstrap step (chunk 0, 2640 x 2640), timed on its own
+    t1 = time.perf_counter()
+    out0, _ = ro.first_chunk_step(0, 0, *data[0])
+    boot_s = time.perf_counter() - t1
+    assert np.isfinite(out0).all()
+    boot_flops = 4 * cfg.tokens(0) * cfg.tokens(0) * heads * cfg.head_dim
+    # extrapolated 1-layer rollout (all heads): chunk 0's 5 calls at the
+    # bootstrap rate, the 112 chunk calls at the steady-state rate (both rates
+    # include the rotation of the call's own q and k)
+    scale = cfg.num_heads / heads
+    boot_rate = boot_flops / boot_s
+    roll_s = sum(attn_flops(cfg, c) / (boot_rate if c == 0 else rate) for _, _, c in rollout_calls(cfg))
     cpu_model = platform.processor() or ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -227,11 +246,17 @@ def cpu_baseline(cfg, heads, calls=6):
     except OSError:
         pass
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": (f"float64 numpy oracle: RoPE of the sink's and chunks 1..18's keys, then chunks "
                    f"19..{last} at step 0 (RoPE, record, attention 880 x 19,360 keys) for {heads} of 24 heads; "
-                   f"{flops / 1e9:.1f} GFLOP in {dt:.2f} s"),
+                   f"{flops / 1e9:.1f} GFLOP in {dt:.2f} s; plus one 2640 x 2640 bootstrap step "
+                   f"({boot_flops / 1e9:.1f} GFLOP in {boot_s:.2f} s)"),
         "seconds": dt, "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
+        "bootstrap_2640x2640_s": round(boot_s * scale, 3),
+        "bootstrap_tflops": round(boot_rate / 1e12, 4),
+        "rollout_1layer_s_extrapolated": round(roll_s, 1),
+        "extrapolation": ("117 attention calls of the 1-layer 29-chunk rollout, each at the measured rate of its "
+                          "kind (rotation included); not timed in full"),
     }
 
 

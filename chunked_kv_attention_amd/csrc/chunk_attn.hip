@@ -33,15 +33,16 @@
 // operand.
 //
 // Softmax.  Scores stay raw; the scale (times log2 e) is folded into one FMA
-// per score before exp2.  The running max is lazy: O and the running sums are
-// rescaled only when a tile raises some row's max by more than 2^8 (a
-// wave-uniform branch), otherwise the stale max is kept and P may reach 256,
-// which bf16 and the fp32 accumulators hold exactly enough.  The test needs
-// no cross-lane max: each lane compares its own raw scores of its query with
-// that query's threshold (m + 8) / (scale log2 e), and the 2-lane max is
-// taken only inside the rare rescale branch.  The row sums add the same
-// bf16-rounded P that multiplies V (v_dot2_f32_bf16 against ones), so
-// numerator and denominator see the same weights.
+// per score before exp2.  The running max is lazy: a tile's weights are
+// computed against the stale max and kept as long as each lane's sum of them
+// stays <= 2^8 (then no weight exceeds 2^8, which bf16 and the fp32
+// accumulators hold exactly enough); only when that sum is larger, NaN or
+// infinite (rare; always on a split's first tile, where the max is -inf) is
+// the 2-lane max taken, O and the running sums rescaled and the tile's
+// weights recomputed.  The check needs no max over the scores of every tile.
+// The row sums add the same bf16-rounded P that multiplies V
+// (v_dot2_f32_bf16 against ones), so numerator and denominator see the same
+// weights.
 //
 // Occupancy.  880 queries x 24 heads is only 168 workgroups of 128 rows for
 // 256 CUs (21 for a 3-head share), so the key range is split into as many
@@ -73,7 +74,7 @@ constexpr int KT = kAttnKeyTile;    // 64
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
-constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr float kTileSumLimit = 256.0f;  // lazy rescale: a lane's tile sum of weights at most 2^8
 constexpr int MB = KT / 32;           // 32-key blocks of S^T per tile
 constexpr int KS = KT / 16;           // 16-key steps of the PV product per tile
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -297,6 +298,26 @@ __device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, 
   }
 }
 
+// P = 2^(s * scale_log2 - m) in bf16 (the PV product's B operand); returns
+// this lane's sum of the same bf16 weights.
+__device__ inline float tile_weights(const f32x16 (&s)[MB], bf16x8 (&pf)[KS], float m, float scale_log2) {
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  const float neg_m = -m;
+  float ts = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], scale_log2, neg_m));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r + 1], scale_log2, neg_m));
+      const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+      ts = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, ts, false);
+      pf[2 * mb + r / 8][r % 8] = pk[0];
+      pf[2 * mb + r / 8][r % 8 + 1] = pk[1];
+    }
+  return ts;
+}
+
 // One key tile for a wave's 32 queries:
 //   S^T = K_tile Q^T, online softmax per query, O^T += V^T_tile P^T.
 // S value (mb)[r] is the score of tile key 32mb + 16(r/8) + 8h + 4((r/4)%2)
@@ -306,7 +327,7 @@ __device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, 
 // step ks.
 template <int D>
 __device__ inline void attend_tile(const char* sk, const char* sv, const int (&ka)[D / 16], const int (&va)[KS],
-                                   const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], float& m, float& thr, float& lsum,
+                                   const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], float& m, float& lsum,
                                    float scale_log2, bool masked, int t0, int key_end, int h) {
   using T = Tile<D>;
   constexpr int KK = D / 16;
@@ -339,12 +360,16 @@ __device__ inline void attend_tile(const char* sk, const char* sv, const int (&k
       for (int r = 0; r < 16; ++r)
         if (t0 + 32 * mb + 16 * (r / 8) + 8 * h + 4 * ((r / 4) % 2) + r % 4 >= key_end) s[mb][r] = -INFINITY;
   }
-  // Rescale test without the cross-lane max: the query needs a new max only
-  // if one of its raw scores exceeds thr = (m + 2^8 headroom) / scale_log2,
-  // and each lane can test its own 32 scores.  The 2-lane max is taken only
-  // in the rare branch.
-  float lm;
-  {
+  // Weights against the running max m, and this lane's share of the tile's
+  // sum of them.  Lazy rescale: the weights are kept while that sum stays
+  // <= 2^8, so every weight is <= 2^8, which bf16 and the float32
+  // accumulators hold exactly enough.  Otherwise (rarely; always on a
+  // split's first tile, where m = -inf makes the sum NaN or inf) the 2-lane
+  // max is taken, O and the running sum are rescaled, and the weights are
+  // recomputed.
+  bf16x8 pf[KS];
+  float ts = tile_weights(s, pf, m, scale_log2);
+  if (__any(!(ts <= kTileSumLimit))) {
     float a[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -357,34 +382,18 @@ __device__ inline void attend_tile(const char* sk, const char* sv, const int (&k
       b2 = max3f(b2, b3, b4);
       a[mb] = max2f(b0, b2);
     }
-    lm = a[0];
+    float lm = a[0];
 #pragma unroll
     for (int mb = 1; mb < MB; ++mb) lm = max2f(lm, a[mb]);
-  }
-  if (__any(lm > thr)) {
     const float m_new = fmaxf(m, pair_max(lm) * scale_log2);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);
     lsum *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
     m = m_new;
-    thr = (m_new + kRescaleLog2) / scale_log2;
+    ts = tile_weights(s, pf, m, scale_log2);
   }
-
-  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x8 pf[KS];
-  const float neg_m = -m;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], scale_log2, neg_m));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r + 1], scale_log2, neg_m));
-      const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, lsum, false);
-      pf[2 * mb + r / 8][r % 8] = pk[0];
-      pf[2 * mb + r / 8][r % 8 + 1] = pk[1];
-    }
+  lsum += ts;
 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -461,7 +470,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = -INFINITY;    // running max of scaled scores (log2 domain)
   float lsum = 0.f;       // this lane's share of the running sum
-  float thr = -INFINITY;  // raw-score level that forces a rescale
 
   fetch_tile<D>(runs, slots, cursor, wave, lane, t_begin * KT, key_begin, key_end, sk0, sv0);
   for (int t = t_begin; t < t_end; t += 2) {
@@ -469,12 +477,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 1 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 1) * KT, key_begin, key_end, sk1, sv1);
-    attend_tile<D>(sk0, sv0, ka, va, qf, o, m, thr, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
+    attend_tile<D>(sk0, sv0, ka, va, qf, o, m, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
     if (t + 1 >= t_end) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 2 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 2) * KT, key_begin, key_end, sk0, sv0);
-    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, thr, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT,
+    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT,
                    key_end, h);
   }
 
