@@ -430,6 +430,46 @@ def attn880x19360(args, heads=24):
     }), flush=True)
 
 
+def appends_back_to_back(C, cfg, dev, stream, inputs, calls, gains=None, reps=4):
+    """RoPE + append (QK-Norm + RoPE + append when `gains` is given) of the
+    880-token chunks 1..28 at step 0, launched back to back into a fresh cache
+    after its sink, with one event pair around the 28 appends (an event
+    between two launches is a queue barrier); per-call time = the pair's time
+    / 28, the median over `reps` - 1 timed repetitions after one warm-up."""
+    import torch
+    H, d = cfg.num_heads, cfg.head_dim
+    cache = C.Cache(cfg)
+    chunk_inputs = {c: inputs[i] for i, (kind, step, c) in enumerate(calls) if kind == "chunk" and step == 0}
+    sink_in = next(inputs[i] for i, (kind, _, _) in enumerate(calls) if kind == "sink")
+    n0, n1 = cfg.tokens(0), cfg.tokens(1)
+    qr0 = torch.empty((n0, H, d), device=dev, dtype=torch.bfloat16)
+    qr1 = torch.empty((n1, H, d), device=dev, dtype=torch.bfloat16)
+    times = []
+    for rep in range(reps):
+        cache.reset()
+        if gains is None:
+            cache.sink_build(0, *sink_in, qr0, stream=stream)
+        else:
+            cache.norm_sink_build(0, *sink_in, *gains, 1e-6, qr0, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for c in range(1, 29):
+            if gains is None:
+                cache.rope_append(0, 0, c, *chunk_inputs[c], qr1, stream=stream)
+            else:
+                cache.norm_rope_append(0, 0, c, *chunk_inputs[c], *gains, 1e-6, qr1, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            times.append(e0.elapsed_time(e1) * 1e3 / 28)
+    times.sort()
+    us = times[len(times) // 2]
+    nbytes = 6 * n1 * H * d * 2
+    return {"us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "timing": "28 appends back to back between one event pair (chunks 1..28, step 0)"}
+
+
 def norm_append_and_copy(C, cfg, dev, stream, inputs, calls):
     """QK-Norm + RoPE + append on the 880-token chunks (its own cache; gains
     seeded), and a plain device copy of the same byte count for context."""
@@ -438,26 +478,8 @@ def norm_append_and_copy(C, cfg, dev, stream, inputs, calls):
     g = torch.Generator(device=dev)
     g.manual_seed(77)
     gains = [1.0 + 0.3 * torch.randn(H * d, generator=g, device=dev, dtype=torch.float32) for _ in range(2)]
-    cache = C.Cache(cfg)
-    chunk_inputs = {c: inputs[i] for i, (kind, step, c) in enumerate(calls) if kind == "chunk" and step == 0}
-    sink_in = next(inputs[i] for i, (kind, _, _) in enumerate(calls) if kind == "sink")
-    n0, n1 = cfg.tokens(0), cfg.tokens(1)
-    qr0 = torch.empty((n0, H, d), device=dev, dtype=torch.bfloat16)
-    qr1 = torch.empty((n1, H, d), device=dev, dtype=torch.bfloat16)
-    times = []
-    for rep in range(4):
-        cache.reset()
-        cache.norm_sink_build(0, *sink_in, *gains, 1e-6, qr0, stream=stream)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(29)]
-        for c in range(1, 29):
-            evs[c - 1].record(stream)
-            cache.norm_rope_append(0, 0, c, *chunk_inputs[c], *gains, 1e-6, qr1, stream=stream)
-        evs[28].record(stream)
-        torch.cuda.synchronize()
-        if rep:
-            times += [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(28)]
-    times.sort()
-    us = times[len(times) // 2]
+    norm = appends_back_to_back(C, cfg, dev, stream, inputs, calls, gains)
+    n1 = cfg.tokens(1)
     nbytes = 6 * n1 * H * d * 2
     # 16 distinct buffer pairs (0.5 GB), so the copies stream from HBM like the appends' fresh inputs
     pairs = [(torch.empty(nbytes // 2, dtype=torch.uint8, device=dev),   # read + write = the append's bytes
@@ -473,9 +495,8 @@ def norm_append_and_copy(C, cfg, dev, stream, inputs, calls):
     torch.cuda.synchronize()
     copy_us = e0.elapsed_time(e1) * 1e3 / 48
     del pairs
-    return ({"us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
-             "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
-             "calls_timed": len(times), "note": "algorithmic bytes as rope_append_880 (the norm adds no pass over q and k)"},
+    norm["note"] = "algorithmic bytes as rope_append_880 (the norm adds no pass over q and k)"
+    return (norm,
             {"bytes_moved": nbytes, "us_per_copy": round(copy_us, 2),
              "gbs": round(nbytes / (copy_us * 1e-6) / 1e9, 1),
              "note": "device-to-device copy moving the append's byte count (half read, half written), event-timed"})
@@ -648,16 +669,30 @@ def main():
         run_rollout()
     torch.cuda.synchronize()
 
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(args.steps)]
+    # Timed rollouts: events only at the two ends (an event recorded between
+    # two launches is a queue barrier that idles the GPU for microseconds).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        run_rollout(events[k])
+        run_rollout()
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
+
+    # The same number of rollouts again, instrumented: event pairs around every
+    # append and attention call give the per-launch figures (roofline, append).
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    i0 = torch.cuda.Event(enable_timing=True)
+    i1 = torch.cuda.Event(enable_timing=True)
+    i0.record(stream)
+    for k in range(args.steps):
+        run_rollout(events[k])
+    i1.record(stream)
+    torch.cuda.synchronize()
+    instrumented_ms = i0.elapsed_time(i1) / args.steps
 
     attn_big_ms = [events[k][i][1].elapsed_time(events[k][i][2]) for k in range(args.steps) for i in big]
     attn_all_ms = sum(events[k][i][1].elapsed_time(events[k][i][2]) for k in range(args.steps)
@@ -705,11 +740,13 @@ def main():
             "launches_timed": len(attn_big_ms),
             "key_splits": cache.attention_splits(880, 19360),
         },
-        "attention_share_of_step": round(attn_all_ms / total_ms, 4),
-        "rope_append_880": {
+        "attention_share_of_step": round(attn_all_ms / (instrumented_ms * args.steps), 4),
+        "ms_per_step_with_per_call_events": round(instrumented_ms, 3),
+        "rope_append_880": appends_back_to_back(C, cfg, dev, stream, inputs, calls),
+        "rope_append_880_event_pairs": {
             "us_per_call": round(append_us, 2),
             "gbs": round(append_bytes / (append_us * 1e-6) / 1e9, 1),
-            "pct_hbm_peak": round(100 * append_bytes / (append_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "timing": "an event pair around every append of the instrumented rollouts (barrier cost included)",
         },
         "roofline": {
             "bound": "mfma",
@@ -722,14 +759,15 @@ def main():
             "launches_timed": args.steps * len(calls),
             "flops_per_launch": attn_flops_per_call,
             "us_per_launch": round(attn_us_per_call, 2),
+            "timing": "HIP event pairs around every attention call of the instrumented rollouts",
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         },
     }
-    # the single call as stated for the 880 x 19,360 shape (peaky keys), and the
-    # 3-head share of 8-way head sharding (4 key splits)
-    result["chunk_attn_880x19360"] = single_call_timing(24)
-    result["chunk_attn_880x19360_3heads"] = single_call_timing(3)
     if not args.no_extras:
+        # the single call as stated for the 880 x 19,360 shape (peaky keys), and
+        # the 3-head share of 8-way head sharding (24 key splits)
+        result["chunk_attn_880x19360"] = single_call_timing(24)
+        result["chunk_attn_880x19360_3heads"] = single_call_timing(3)
         result["norm_rope_append_880"], result["device_copy_same_bytes"] = norm_append_and_copy(
             C, cfg, dev, stream, inputs, calls)
         result["cross_attn_880x512"] = cross_attention_timing(C, cfg, dev, stream)
