@@ -159,7 +159,8 @@ def summarise_counters(fetch_csv, write_csv):
     write_bytes = sum(k for _, _, k in w_attn) * 1024 * write_scale / calls
     lines = [
         "# HBM traffic of one chunk-attention call (chunk_attn_kernel + attn_combine_kernel),",
-        "# averaged over the 117 calls of one 1-layer 29-chunk rollout.",
+        "# averaged over every attention call of the profiled run (its timed and its instrumented",
+        "# 1-layer 29-chunk rollout, 117 calls each).",
         "# Commands (run from the repository root; cd /tmp && export TMPDIR=/tmp first):",
         "#   rocprofv3 --pmc FETCH_SIZE -d OUT_F -o fetch --output-format csv -- "
         "python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras --copy-calibration",
