@@ -33,16 +33,21 @@
 // operand.
 //
 // Softmax.  Scores stay raw; the scale (times log2 e) is folded into one FMA
-// per score before exp2.  The running max is lazy: a tile's weights are
-// computed against the stale max and kept as long as each lane's sum of them
-// stays <= 2^8 (then no weight exceeds 2^8, which bf16 and the fp32
-// accumulators hold exactly enough); only when that sum is larger, NaN or
-// infinite (rare; always on a split's first tile, where the max is -inf) is
-// the 2-lane max taken, O and the running sums rescaled and the tile's
-// weights recomputed.  The check needs no max over the scores of every tile.
-// The row sums add the same bf16-rounded P that multiplies V
-// (v_dot2_f32_bf16 against ones), so numerator and denominator see the same
-// weights.
+// per score before exp2.  A tile is taken as two 32-key blocks so that one
+// block's softmax runs on the vector ALUs while the matrix units work on the
+// other: S^T of block 1 is issued before block 0's weights, and block 0's
+// PV steps before block 1's weights (scheduling-group barriers interleave
+// them).  The running max is lazy, per block: a block's weights are computed
+// against the stale max and kept as long as each lane's sum of them stays
+// <= 2^8 (then no weight exceeds 2^8, which bf16 and the fp32 accumulators
+// hold exactly enough); only when that sum is larger, NaN or infinite (rare;
+// always on a split's first block, where the max is -inf) is the block's
+// 2-lane max taken, O and the running sums rescaled and the block's weights
+// recomputed.  The check needs no max over the scores of every block.  The
+// row sums add the same bf16-rounded P that multiplies V (v_dot2_f32_bf16
+// against ones), so numerator and denominator see the same weights.  Only
+// the last tile of a split can be partial; it runs after the loop with a
+// masked copy of the tile code, so the loop carries one copy.
 //
 // Occupancy.  880 queries x 24 heads is only 168 workgroups of 128 rows for
 // 256 CUs (21 for a 3-head share), so the key range is split into as many
@@ -75,7 +80,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
 constexpr float kTileSumLimit = 256.0f;  // lazy rescale: a lane's tile sum of weights at most 2^8
-constexpr int MB = KT / 32;           // 32-key blocks of S^T per tile
+static_assert(KT == 64, "a key tile is two 32-key blocks");
 constexpr int KS = KT / 16;           // 16-key steps of the PV product per tile
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
@@ -298,118 +303,160 @@ __device__ inline void fetch_tile(const Runs& R, LaneSlots<D>& s, RunCursor& c, 
   }
 }
 
-// P = 2^(s * scale_log2 - m) in bf16 (the PV product's B operand); returns
-// this lane's sum of the same bf16 weights.
-__device__ inline float tile_weights(const f32x16 (&s)[MB], bf16x8 (&pf)[KS], float m, float scale_log2) {
+constexpr int kSchedValu = 0x002;
+
+// P = 2^(s * scale_log2 - m) in bf16 for one 32-key block (the B operands of
+// its two 16-key PV steps); returns this lane's sum of the same bf16 weights.
+__device__ inline float block_weights(const f32x16& s, bf16x8& p0, bf16x8& p1, float m, float scale_log2) {
   const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
   const float neg_m = -m;
   float ts = 0.f;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], scale_log2, neg_m));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r + 1], scale_log2, neg_m));
-      const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-      ts = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, ts, false);
-      pf[2 * mb + r / 8][r % 8] = pk[0];
-      pf[2 * mb + r / 8][r % 8 + 1] = pk[1];
+  for (int r = 0; r < 16; r += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, neg_m));
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, neg_m));
+    const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+    ts = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, ts, false);
+    if (r < 8) {
+      p0[r] = pk[0];
+      p0[r + 1] = pk[1];
+    } else {
+      p1[r - 8] = pk[0];
+      p1[r - 7] = pk[1];
     }
+  }
   return ts;
 }
 
+// Rare path of the lazy rescale: raise m to the block's 2-lane max (log2
+// domain) and rescale O and the running sum to it.
+template <int DB>
+__device__ inline void rescale_to_block(const f32x16& s, f32x16 (&o)[DB], float& m, float& lsum, float scale_log2) {
+  float b0 = max3f(s[0], s[1], s[2]);
+  float b1 = max3f(s[3], s[4], s[5]);
+  float b2 = max3f(s[6], s[7], s[8]);
+  float b3 = max3f(s[9], s[10], s[11]);
+  float b4 = max3f(s[12], s[13], s[14]);
+  b0 = max3f(b0, b1, s[15]);
+  b2 = max3f(b2, b3, b4);
+  const float m_new = fmaxf(m, pair_max(max2f(b0, b2)) * scale_log2);
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  lsum *= alpha;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  m = m_new;
+}
+
 // One key tile for a wave's 32 queries:
-//   S^T = K_tile Q^T, online softmax per query, O^T += V^T_tile P^T.
-// S value (mb)[r] is the score of tile key 32mb + 16(r/8) + 8h + 4((r/4)%2)
-// + r%4 (h = lane / 32) for query lane % 32.  O value (db)[r] is head dim
-// 32db + 8(r/4) + 4h + r%4 of that query.  ka[kk] / va[ks] are this lane's
-// operand byte offsets within a K / V^T tile for 16-dim step kk / 16-key
-// step ks.
-template <int D>
+//   S^T = K_tile Q^T, online softmax per query, O^T += V^T_tile P^T,
+// taken as two 32-key blocks so that each block's softmax runs while the
+// matrix units work on the other: S^T of block 1 is issued before the
+// weights of block 0 are computed, and the PV steps of block 0 before the
+// weights of block 1.  Each block has its own lazy-rescale check.
+// S value [r] of block mb is the score of tile key 32mb + 16(r/8) + 8h +
+// 4((r/4)%2) + r%4 (h = lane / 32) for query lane % 32.  O value (db)[r] is
+// head dim 32db + 8(r/4) + 4h + r%4 of that query.  ka[kk] / va[ks] are this
+// lane's operand byte offsets within a K / V^T tile for 16-dim step kk /
+// 16-key step ks.
+template <int D, bool kMasked>
 __device__ inline void attend_tile(const char* sk, const char* sv, const int (&ka)[D / 16], const int (&va)[KS],
                                    const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], float& m, float& lsum,
-                                   float scale_log2, bool masked, int t0, int key_end, int h) {
+                                   float scale_log2, int t0, int key_end, int h) {
   using T = Tile<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
-  f32x16 s[MB];
+  constexpr int kWeightValu = 48 / KK;  // VALU of one block's weights per MFMA it hides behind
+  f32x16 s0, s1;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = 0.f;
+    s1[r] = 0.f;
+  }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sk + ka[kk]));
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s0, 0, 0, 0);
+  }
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sk + 32 * T::kRowBytesK + ka[kk]));
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s1, 0, 0, 0);
+  }
+  if (kMasked) {
+    // keys of this lane's scores past key_end get -inf; the bound is formed
+    // here and hidden from the optimiser so that nothing per score is hoisted
+    // out of the key loop
+    int lim = key_end - t0 - 8 * h;
+    opaque(lim);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sk + mb * 32 * T::kRowBytesK + ka[kk]));
-      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
+    for (int r = 0; r < 16; ++r) {
+      const int k0 = 16 * (r / 8) + 4 * ((r / 4) % 2) + r % 4;
+      if (k0 >= lim) s0[r] = -INFINITY;
+      if (k0 + 32 >= lim) s1[r] = -INFINITY;
     }
-  // Keep the K operand reads 4 ahead of the MFMAs that consume them (LDS
-  // latency spans a few MFMAs).
+  }
+  bf16x8 pf[KS];
+  float ts = block_weights(s0, pf[0], pf[1], m, scale_log2);
+  // K operand reads 4 ahead of their MFMAs; block 0's weights between block
+  // 1's MFMAs
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-  for (int j = 0; j < MB * KK - 4; ++j) {
+  for (int j = 0; j < KK; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-  if (masked) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (t0 + 32 * mb + 16 * (r / 8) + 8 * h + 4 * ((r / 4) % 2) + r % 4 >= key_end) s[mb][r] = -INFINITY;
+  for (int j = 0; j < KK; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (j < KK - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kWeightValu, 0);
   }
-  // Weights against the running max m, and this lane's share of the tile's
-  // sum of them.  Lazy rescale: the weights are kept while that sum stays
+  // Lazy rescale: the weights are kept while this lane's sum of them stays
   // <= 2^8, so every weight is <= 2^8, which bf16 and the float32
   // accumulators hold exactly enough.  Otherwise (rarely; always on a
-  // split's first tile, where m = -inf makes the sum NaN or inf) the 2-lane
-  // max is taken, O and the running sum are rescaled, and the weights are
-  // recomputed.
-  bf16x8 pf[KS];
-  float ts = tile_weights(s, pf, m, scale_log2);
+  // split's first block, where m = -inf makes the sum NaN or inf) O and the
+  // running sum are rescaled to the block's max and the weights recomputed.
   if (__any(!(ts <= kTileSumLimit))) {
-    float a[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float b0 = max3f(s[mb][0], s[mb][1], s[mb][2]);
-      float b1 = max3f(s[mb][3], s[mb][4], s[mb][5]);
-      float b2 = max3f(s[mb][6], s[mb][7], s[mb][8]);
-      float b3 = max3f(s[mb][9], s[mb][10], s[mb][11]);
-      float b4 = max3f(s[mb][12], s[mb][13], s[mb][14]);
-      b0 = max3f(b0, b1, s[mb][15]);
-      b2 = max3f(b2, b3, b4);
-      a[mb] = max2f(b0, b2);
-    }
-    float lm = a[0];
-#pragma unroll
-    for (int mb = 1; mb < MB; ++mb) lm = max2f(lm, a[mb]);
-    const float m_new = fmaxf(m, pair_max(lm) * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    lsum *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    m = m_new;
-    ts = tile_weights(s, pf, m, scale_log2);
+    rescale_to_block<DB>(s0, o, m, lsum, scale_log2);
+    ts = block_weights(s0, pf[0], pf[1], m, scale_log2);
   }
   lsum += ts;
 
+  // PV steps of block 0, block 1's weights between them; block 1's V^T
+  // operands are read here too, so that its PV steps after the check issue
+  // without waiting for LDS
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sv + db * 32 * T::kRowBytesV + va[ks]));
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
     }
-  // same read-ahead for the V^T operands
+  bf16x8 vb[2][DB];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vb[ks][db] = as_bf16x8(*reinterpret_cast<const uint4*>(sv + db * 32 * T::kRowBytesV + va[2 + ks]));
+  ts = block_weights(s1, pf[2], pf[3], m, scale_log2);
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
-  for (int j = 0; j < KS * DB - 4; ++j) {
+  for (int j = 0; j < 2 * DB; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+    // the other 4 DB - 4 operand reads, two after each MFMA while they last
+    if (4 * DB - 4 - 2 * j >= 2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+    else if (4 * DB - 4 - 2 * j == 1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 48 / (2 * DB), 1);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+  if (__any(!(ts <= kTileSumLimit))) {
+    rescale_to_block<DB>(s1, o, m, lsum, scale_log2);
+    ts = block_weights(s1, pf[2], pf[3], m, scale_log2);
+  }
+  lsum += ts;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[ks][db], pf[2 + ks], o[db], 0, 0, 0);
 }
 
 template <int D>
@@ -472,18 +519,35 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
   float lsum = 0.f;       // this lane's share of the running sum
 
   fetch_tile<D>(runs, slots, cursor, wave, lane, t_begin * KT, key_begin, key_end, sk0, sv0);
-  for (int t = t_begin; t < t_end; t += 2) {
+  // Tiles [t_begin, t_full) are whole: they run in pairs (buffer 0, then
+  // buffer 1), then a last whole tile if their count is odd; a partial last
+  // tile (keys up to key_end) runs after them with the masked copy of the
+  // tile code, in the buffer its parity gives.
+  const int t_full = min(key_end / KT, t_end);
+  int t = t_begin;
+  for (; t + 1 < t_full; t += 2) {
     // buffer 0 holds tile t; tile t+1 goes to buffer 1 while t is computed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 1) * KT, key_begin, key_end, sk1, sv1);
-    attend_tile<D>(sk0, sv0, ka, va, qf, o, m, lsum, p.scale_log2, t * KT + KT > key_end, t * KT, key_end, h);
-    if (t + 1 >= t_end) break;
+    fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 1) * KT, key_begin, key_end, sk1, sv1);
+    attend_tile<D, false>(sk0, sv0, ka, va, qf, o, m, lsum, p.scale_log2, t * KT, key_end, h);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 2 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 2) * KT, key_begin, key_end, sk0, sv0);
-    attend_tile<D>(sk1, sv1, ka, va, qf, o, m, lsum, p.scale_log2, (t + 1) * KT + KT > key_end, (t + 1) * KT,
-                   key_end, h);
+    attend_tile<D, false>(sk1, sv1, ka, va, qf, o, m, lsum, p.scale_log2, (t + 1) * KT, key_end, h);
+  }
+  if (t < t_full) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < t_end) fetch_tile<D>(runs, slots, cursor, wave, lane, (t + 1) * KT, key_begin, key_end, sk1, sv1);
+    attend_tile<D, false>(sk0, sv0, ka, va, qf, o, m, lsum, p.scale_log2, t * KT, key_end, h);
+    ++t;
+  }
+  if (t < t_end) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const bool odd = ((t - t_begin) & 1) != 0;
+    attend_tile<D, true>(odd ? sk1 : sk0, odd ? sv1 : sv0, ka, va, qf, o, m, lsum, p.scale_log2, t * KT, key_end, h);
   }
 
   const float ltot = pair_sum(lsum);
@@ -518,63 +582,75 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
   }
 }
 
-// Merge of the key splits: O = sum_j 2^(lse_j - M) O_j / sum_j 2^(lse_j - M).
-template <int D>
+// Merge of the key splits: O = sum_j 2^(lse_j - M) O_j / sum_j 2^(lse_j - M),
+// M = max_j lse_j.  A thread takes 8 dims (16 bytes of each fp16 partial) of
+// one (query, head) row and loads every split's log-sum-exp and partial
+// before it uses any (MaxSplits bounds n_splits), so a row costs two memory
+// round trips whatever the split count.
+template <int D, int MaxSplits>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
-  constexpr int TPR = D / 4;  // threads per (query, head) row
+  constexpr int TPR = D / 8;  // threads per (query, head) row
   const long long rows = (long long)p.n_queries * p.num_heads;
   const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= rows) return;
-  const int c4 = threadIdx.x % TPR;
-  float mx = -INFINITY;
-  for (int j = 0; j < p.n_splits; ++j) mx = fmaxf(mx, p.part_lse[j * rows + row]);
+  const int c8 = threadIdx.x % TPR;
+  float lse[MaxSplits];
+#pragma unroll
+  for (int j = 0; j < MaxSplits; ++j) lse[j] = j < p.n_splits ? p.part_lse[j * rows + row] : -INFINITY;
+  uint4 part[MaxSplits];
+#pragma unroll
+  for (int j = 0; j < MaxSplits; ++j)
+    part[j] = j < p.n_splits ? *reinterpret_cast<const uint4*>(p.part_o + (j * rows + row) * D + 8 * c8)
+                             : make_uint4(0, 0, 0, 0);
+  float mx = lse[0];
+#pragma unroll
+  for (int j = 1; j < MaxSplits; ++j) mx = fmaxf(mx, lse[j]);
   float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // four splits' values in flight at a time
-  for (int j0 = 0; j0 < p.n_splits; j0 += 4) {
-    float w[4];
-    float4 v[4];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = j0 + i;
-      const bool on = j < p.n_splits;
-      w[i] = on ? __builtin_amdgcn_exp2f(p.part_lse[j * rows + row] - mx) : 0.f;
-      if (on) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p.part_o + (j * rows + row) * D + 4 * c4);
-        const half2 lo = __builtin_bit_cast(half2, u.x), hi = __builtin_bit_cast(half2, u.y);
-        v[i] = make_float4((float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]);
-      } else {
-        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
+  for (int j = 0; j < MaxSplits; ++j) {
+    const float w = j < p.n_splits ? __builtin_amdgcn_exp2f(lse[j] - mx) : 0.f;
+    wsum += w;
+    const uint32_t words[4] = {part[j].x, part[j].y, part[j].z, part[j].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wsum += w[i];
-      acc.x += w[i] * v[i].x;
-      acc.y += w[i] * v[i].y;
-      acc.z += w[i] * v[i].z;
-      acc.w += w[i] * v[i].w;
+    for (int e = 0; e < 4; ++e) {
+      const half2 v = __builtin_bit_cast(half2, words[e]);
+      acc[2 * e] += w * (float)v[0];
+      acc[2 * e + 1] += w * (float)v[1];
     }
   }
   const float inv = 1.f / wsum;
-  const bf16x2 lo = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv)};
-  const bf16x2 hi = {(__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
-  *reinterpret_cast<uint2*>(p.out + row * D + 4 * c4) =
-      make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+  uint32_t packed[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 b = {(__bf16)(acc[2 * e] * inv), (__bf16)(acc[2 * e + 1] * inv)};
+    packed[e] = __builtin_bit_cast(uint32_t, b);
+  }
+  *reinterpret_cast<uint4*>(p.out + row * D + 8 * c8) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
+template <int D>
+void launch_combine(const AttnParams& p, hipStream_t s) {
+  const int blocks = (int)(((long long)p.n_queries * p.num_heads * (D / 8) + 255) / 256);
+  if (p.n_splits <= 4)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 4>), dim3(blocks), dim3(256), 0, s, p);
+  else if (p.n_splits <= 8)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 8>), dim3(blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, kAttnMaxSplits>), dim3(blocks), dim3(256), 0, s, p);
 }
 
 }  // namespace
 
 hipError_t launch_chunk_attention(const AttnParams& p, int head_dim, hipStream_t s) {
-  if (p.n_queries <= 0 || p.n_keys <= 0 || p.n_splits < 1) return hipErrorInvalidValue;
+  if (p.n_queries <= 0 || p.n_keys <= 0 || p.n_splits < 1 || p.n_splits > kAttnMaxSplits) return hipErrorInvalidValue;
   const int units = p.q_tiles * p.num_heads * p.n_splits;
-  const int combine_blocks = (int)(((long long)p.n_queries * p.num_heads * (head_dim / 4) + 255) / 256);
   if (head_dim == 128) {
     hipLaunchKernelGGL(chunk_attn_kernel<128>, dim3(units), dim3(kThreads), 0, s, p);
-    if (p.n_splits > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(combine_blocks), dim3(256), 0, s, p);
+    if (p.n_splits > 1) launch_combine<128>(p, s);
   } else if (head_dim == 64) {
     hipLaunchKernelGGL(chunk_attn_kernel<64>, dim3(units), dim3(kThreads), 0, s, p);
-    if (p.n_splits > 1) hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(combine_blocks), dim3(256), 0, s, p);
+    if (p.n_splits > 1) launch_combine<64>(p, s);
   } else {
     return hipErrorInvalidValue;
   }
