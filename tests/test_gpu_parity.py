@@ -350,6 +350,24 @@ def test_ragged_query_and_key_tiles_two_layers():
     r.run_chunks(range(1, 10))
 
 
+def test_partial_last_tile_in_either_buffer():
+    """Windows of 64 .. 208 keys in steps of 16 (4 x 4 grid, window 9, one
+    split): whole tiles only (64, 128, 192 keys), one whole tile then a
+    partial one (80 .. 112: the partial tile sits in the second LDS buffer),
+    two whole tiles then a partial one (144 .. 176: first buffer) and three
+    whole tiles then a partial one (208: the odd leftover whole tile, then
+    the second buffer); every output element of every call."""
+    cfg = C.Config(1, 1, 2, 64, 4, 4, 3, 9, 13)
+    r = G.Rollout(cfg, base_seed=12)
+    keys = [48 + 16 * min(c - 1, 9) + 16 for c in range(1, 13)]
+    assert sorted(set(k % 64 for k in keys)) == [0, 16, 32, 48]
+    assert {k // 64 for k in keys if k % 64} == {1, 2, 3}
+    assert all(r.cache.attention_splits(16, k) == 1 for k in keys)
+    r.run_first_chunk()
+    r.run_chunks(range(1, 13))
+    print(f"partial tiles: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
+
+
 def test_split_keys_path_head_dim_64():
     """A shape where the key range is split (and merged) with head_dim 64:
     8 x 8 frames, window 14 chunks, so the later windows reach 1,152 keys (18
