@@ -14,8 +14,8 @@
 //
 // QK-Norm ("Learning Video Generation from the Wan2.2 Source Code", Chapter 4,
 // "3D RoPE" detail paragraph: q and k each pass an RMSNorm after their linear
-// layers), when asked for: the wave that rotates a token's q and k holds all
-// of its H*d values, so it takes their mean of squares (float32, a wave
+// layers), when asked for: the wave that rotates a token's q (or its k) holds
+// all of its H*d values, so it takes their mean of squares (float32, a wave
 // reduction), scales each value by 1/sqrt(mean + eps) and its channel's gain,
 // rounds to bf16 (the norm's output precision) and rotates that -- the norm
 // costs no extra pass over q and k.
@@ -121,12 +121,12 @@ constexpr int kGroup = 8;  // 16-byte chunks a lane holds at once (512 per wave)
 
 // Two kinds of workgroup in one launch.
 //  * The first qk_blocks rotate q and k.  Without the QK-Norm: one thread per
-//    16-byte chunk (flat over token x chunk).  With it: one wave per token,
-//    covering q and k of all heads
-//    (the token's whole projected vector, H*d values): consecutive lanes take
-//    consecutive 16-byte chunks, so loads and stores are fully coalesced, and
-//    with the QK-Norm the wave holds every value of the token for its mean of
-//    squares (a wave reduction) before it scales, rounds and rotates.
+//    16-byte chunk (flat over token x chunk).  With it: one wave per token
+//    and tensor, covering q (or k) of all heads (the token's whole projected
+//    vector, H*d values): consecutive lanes take consecutive 16-byte chunks,
+//    so loads and stores are fully coalesced, and the wave holds every value
+//    for the mean of squares (a wave reduction) before it scales, rounds and
+//    rotates.
 //  * The rest: V^T for 64 tokens of one head, transposed through LDS.
 template <int D, bool kNorm>
 __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeAppendParams p, int qk_blocks) {
@@ -164,7 +164,11 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeAppendParams 
     return;
   }
   if (kNorm && (int)blockIdx.x < qk_blocks) {
-    const int tok = blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+    // one wave per (token, tensor): q and k of a token are normalised on
+    // their own, so two waves share the token
+    const int g = blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+    const int tok = g >> 1;
+    const bool is_k = (g & 1) != 0;
     const int lane = threadIdx.x % 64;
     if (tok >= p.n_tokens) return;  // no barrier on this path
     const int per_frame = p.grid_h * p.grid_w;
@@ -175,52 +179,37 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeAppendParams 
     const int frame = p.first_frame + fl;
     const int W8 = H * C8;                    // chunks per token
     const long long base = (long long)tok * H * D;
-    float inv_q = 1.f, inv_k = 1.f;
-    if (kNorm && W8 > 64 * kGroup) {          // wide tokens: a first pass for the norm
-      float sq = 0.f, sk = 0.f;
-      for (int c = lane; c < W8; c += 64) {
-        sq += sum_sq8(*reinterpret_cast<const uint4*>(p.q + base + c * 8));
-        sk += sum_sq8(*reinterpret_cast<const uint4*>(p.k + base + c * 8));
-      }
-      inv_q = 1.f / sqrtf(wave_sum(sq) / (H * D) + p.eps);
-      inv_k = 1.f / sqrtf(wave_sum(sk) / (H * D) + p.eps);
+    const uint16_t* src = is_k ? p.k : p.q;
+    const float* gain = is_k ? p.k_gain : p.q_gain;
+    float inv = 1.f;
+    if (W8 > 64 * kGroup) {                   // wide tokens: a first pass for the norm
+      float sq = 0.f;
+      for (int c = lane; c < W8; c += 64) sq += sum_sq8(*reinterpret_cast<const uint4*>(src + base + c * 8));
+      inv = 1.f / sqrtf(wave_sum(sq) / (H * D) + p.eps);
     }
     for (int g0 = 0; g0 < W8; g0 += 64 * kGroup) {
-      uint4 qv[kGroup], kv[kGroup];
+      uint4 xv[kGroup];
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
         const int c = g0 + lane + 64 * i;
-        if (c < W8) {
-          qv[i] = *reinterpret_cast<const uint4*>(p.q + base + c * 8);
-          kv[i] = *reinterpret_cast<const uint4*>(p.k + base + c * 8);
-        }
+        if (c < W8) xv[i] = *reinterpret_cast<const uint4*>(src + base + c * 8);
       }
-      if (kNorm && W8 <= 64 * kGroup) {
-        float sq = 0.f, sk = 0.f;
+      if (W8 <= 64 * kGroup) {
+        float sq = 0.f;
 #pragma unroll
         for (int i = 0; i < kGroup; ++i)
-          if (g0 + lane + 64 * i < W8) {
-            sq += sum_sq8(qv[i]);
-            sk += sum_sq8(kv[i]);
-          }
-        inv_q = 1.f / sqrtf(wave_sum(sq) / (H * D) + p.eps);
-        inv_k = 1.f / sqrtf(wave_sum(sk) / (H * D) + p.eps);
+          if (g0 + lane + 64 * i < W8) sq += sum_sq8(xv[i]);
+        inv = 1.f / sqrtf(wave_sum(sq) / (H * D) + p.eps);
       }
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
         const int c = g0 + lane + 64 * i;
         if (c < W8) {
           const int head = c / C8, cc = c % C8;
-          uint4 qn = qv[i], kn = kv[i];
-          if (kNorm) {
-            qn = norm8(qn, inv_q, p.q_gain + c * 8);  // channel c*8.. = head*d + 8*cc..
-            kn = norm8(kn, inv_k, p.k_gain + c * 8);
-          }
-          uint4 qo, ko;
-          rotate8<D>(qn, qo, cc * 4, frame, row, col, tab_t, tab_h, tab_w);
-          rotate8<D>(kn, ko, cc * 4, frame, row, col, tab_t, tab_h, tab_w);
-          store_nt(qo, p.q_rot + base + c * 8);
-          store_nt(ko, p.k_dst + head * p.k_head_stride + (long long)tok * D + cc * 8);
+          uint4 xo;
+          rotate8<D>(norm8(xv[i], inv, gain + c * 8), xo, cc * 4, frame, row, col, tab_t, tab_h, tab_w);
+          // channel c*8.. = head*d + 8*cc..
+          store_nt(xo, is_k ? p.k_dst + head * p.k_head_stride + (long long)tok * D + cc * 8 : p.q_rot + base + c * 8);
         }
       }
     }
@@ -343,10 +332,10 @@ __global__ __launch_bounds__(256) void copy_kv_kernel(CopyKVParams p) {
 hipError_t launch_rope_append(const RopeAppendParams& p, int head_dim, hipStream_t s) {
   if (p.n_tokens <= 0 || p.num_heads <= 0) return hipErrorInvalidValue;
   const bool norm = p.q_gain != nullptr;
-  // the norm needs a token's whole vector in one wave; the plain rotation is a
-  // flat grid over 16-byte chunks
+  // the norm needs a token's whole q (or k) vector in one wave: two waves per
+  // token; the plain rotation is a flat grid over 16-byte chunks
   const long long chunks = (long long)p.n_tokens * p.num_heads * (head_dim / 8);
-  const int qk_blocks = norm ? (p.n_tokens + kThreads / 64 - 1) / (kThreads / 64) : (int)((chunks + kThreads - 1) / kThreads);
+  const int qk_blocks = norm ? (2 * p.n_tokens + kThreads / 64 - 1) / (kThreads / 64) : (int)((chunks + kThreads - 1) / kThreads);
   const int v_blocks = ((p.n_tokens + kTok - 1) / kTok) * p.num_heads;
   const dim3 grid(qk_blocks + v_blocks);
   if (head_dim == 128 && norm)
