@@ -3,7 +3,8 @@ allocate: its split partials live in the library's static device array)
 against ckv_chunk_attention on the same cache state, through the C-ABI: two
 calls in a row, the second with a smaller input.  Both run the same kernels
 with the same split, so their outputs must agree bit for bit (beyond the
-attention bar of max |diff| <= 2e-2, rel-L2 <= 5e-3 against each other)."""
+attention bar of max |diff| <= 2e-2, rel-L2 <= 5e-3 against each other).
+Also the call captured into a HIP graph and replayed."""
 
 import numpy as np
 import pytest
@@ -54,3 +55,32 @@ def test_static_scratch_matches_arena_scratch_two_calls():
     # second call, smaller: 128 queries x 2,304 keys at head_dim 64 (4 splits)
     small = C.Config(1, 1, 2, 64, 8, 16, 3, 14, 17)
     assert _compare(small, 15, seed=32) == 4
+
+
+def test_static_entry_point_replays_under_graph_capture():
+    """The callers the entry point is for capture it into a HIP graph: one
+    call (3 heads x 880 x 19,360, 24 key splits and the merge) captured, then
+    replayed three times with the program's own eager work and
+    synchronisations between the replays; every replay must equal the eager
+    call bit for bit."""
+    G.require_gpu()
+    cfg = C.Config(1, 1, 3, 128, 22, 40, 3, 18, 29)
+    cache, q_rot = _fill(cfg, 19, seed=33)
+    eager = torch.empty_like(q_rot)
+    cache.chunk_attention_static(0, 0, 19, q_rot, eager)
+    torch.cuda.synchronize()
+    want = G.bits_of(eager)
+    out = torch.full_like(q_rot, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cache.chunk_attention_static(0, 0, 19, q_rot, out)
+    other = torch.empty_like(q_rot)
+    for replay in range(3):
+        out.fill_(float("nan"))
+        cache.chunk_attention(0, 0, 19, q_rot, other)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"  graph replay {replay}", flush=True)
+        np.testing.assert_array_equal(G.bits_of(out), want)
+    np.testing.assert_array_equal(G.bits_of(other), want)
