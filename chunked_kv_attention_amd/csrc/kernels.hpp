@@ -122,7 +122,8 @@ constexpr int kConvChannelTile = 128;  // output channels per workgroup
 constexpr int kAttnQueryTile = 128;  // query rows per workgroup
 constexpr int kAttnKeyTile = 64;     // keys per LDS tile
 constexpr int kAttnMaxSplits = 32;   // most key splits of one call
-// Rows (query, head) of float32 partials the split scratch holds: every split
+// Rows (query, head) of partials (an fp16 output row and a float32
+// log-sum-exp each) the split scratch holds: every split
 // workgroup of a call owns one query tile of one head, and a call is split
 // only while its workgroups fit the chip's 2-per-CU slots once, so 2 x 256
 // CUs x 128 rows bound every split call on MI355X.

@@ -1,7 +1,7 @@
 // The library's own split scratch, for callers that cannot allocate.
 //
 // ckv_chunk_attention_static runs the same kernels as ckv_chunk_attention but
-// keeps the float32 partial outputs and log-sum-exps of a split call in this
+// keeps the fp16 partial outputs and float32 log-sum-exps of a split call in this
 // file-scope device array instead of the cache arena, so a caller can issue
 // it with nothing allocated for it.  Each GPU the library runs on holds its
 // own copy of the array until the process ends; every call on a GPU shares
