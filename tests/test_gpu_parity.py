@@ -289,6 +289,22 @@ def test_single_chunk_880x19360_peaky():
     assert splits > 1  # the split-key path and its merge are exercised
 
 
+def test_single_chunk_880x19360_head_dim_64():
+    """The head_dim-64 kernel at the full window: 24 heads x 64, chunk 19
+    against 2640 + 18 x 880 + 880 = 19,360 keys (N(0,1) keys), sampled rows
+    over every query tile, both oracles at the bar."""
+    cfg = C.Config(1, 1, 24, 64, 22, 40, 3, 18, 29)
+    r = G.Rollout(cfg, base_seed=21, rows_per_call=64)
+    r.step("sink", 0, 0, 0, check=False)
+    for c in range(1, 19):
+        r.step("chunk", 0, 0, c, check=False)
+    mx, rl2 = r.step("chunk", 0, 0, 19)
+    splits = r.cache.attention_splits(880, 19360)
+    print(f"880x19360 d=64: max abs {mx:.3e} rel L2 {rl2:.3e} (splits {splits}); against unrounded float64 "
+          f"q/k: max abs {r.worst64[0]:.3e} rel L2 {r.worst64[1]:.3e}")
+    assert splits > 1
+
+
 def test_many_key_splits_three_heads_880x19360():
     """One GPU's share of 24 heads sharded 8 ways ("Learning Video Generation
     from the Wan2.2 Source Code", Ch.8, Ulysses: split heads, not the
