@@ -26,7 +26,9 @@ launches.
 x 2 prompts on 2 streams); `--workload attn880x19360` times the chunk-19
 attention call alone, for per-kernel counter runs; `--workload
 conv88x160x384` / `conv44x80x384` time one streaming causal Conv3d layer of
-the VAE decoder (also reported as extras of the default line).
+the VAE decoder (also reported as extras of the default line);
+`--workload vendor_reference` times the platform's own bf16 GEMM (hipBLASLt)
+and fused attention (torch SDPA) on the same GPU, for context.
 
 `--counters FETCH.csv WRITE.csv` turns two rocprofv3 --pmc runs of
 `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras --copy-calibration` (one for
@@ -69,12 +71,13 @@ def parse():
                     help="skip the QK-Norm append, cross-attention and copy lines (profiling runs: only the "
                          "rollout's launches are traced)")
     ap.add_argument("--workload", choices=["rollout1", "rollout30x2", "attn880x19360", "attn3x880x19360",
-                                           "conv88x160x384", "conv44x80x384"], default="rollout1",
+                                           "conv88x160x384", "conv44x80x384", "vendor_reference"], default="rollout1",
                     help="rollout1: 1-layer 29-chunk rollout (default); rollout30x2: 30 layers x 2 prompts on "
                          "2 streams; attn880x19360: the peaky chunk-19 attention call alone, --steps times (for "
                          "per-kernel counter runs); attn3x880x19360: the same call for 3 heads (one GPU's share "
                          "of 8-way head sharding); conv88x160x384 / conv44x80x384: one streaming causal Conv3d "
-                         "layer of the VAE decoder alone")
+                         "layer of the VAE decoder alone; vendor_reference: a hipBLASLt bf16 GEMM and torch's "
+                         "fused SDPA on the 880 x 19,360 shape, for context")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the counters file and exit")
     return ap.parse_args()
@@ -594,6 +597,61 @@ def conv_workload(args):
     }), flush=True)
 
 
+def vendor_reference(args):
+    """`--workload vendor_reference`: the platform's own libraries on the same
+    GPU, for context beside the nominal peak: a plain bf16 GEMM (torch.mm on
+    contiguous 8192 x 8192 operands, i.e. hipBLASLt) and torch's fused
+    scaled_dot_product_attention on the 880-query x 19,360-key x 24-head x
+    128 shape with contiguous bf16 Q, K, V.  Only the flash and
+    memory-efficient backends are allowed (the math backend would run batched
+    products over transposed bf16 views).  Event-timed, `--steps` (at least
+    20) calls after `--warmup` (at least 3)."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    reps, warm = max(args.steps, 20), max(args.warmup, 3)
+
+    def timed(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        return 1e3 * start.elapsed_time(stop) / reps
+
+    n = 8192
+    a, b = (torch.randn((n, n), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2))
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    us_mm = timed(lambda: torch.mm(a, b, out=c))
+    del a, b, c
+    H, d, nq, nk = 24, 128, 880, 19360
+    q = torch.randn((1, H, nq, d), generator=gen, device=dev).to(torch.bfloat16)
+    k, v = (torch.randn((1, H, nk, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2))
+    with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+        us_sdpa = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v))
+    attn = 4 * nq * nk * H * d
+    mm_tflops = 2 * n ** 3 / (us_mm * 1e-6) / 1e12
+    sdpa_tflops = attn / (us_sdpa * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "vendor library bf16 throughput (context)", "value": round(mm_tflops, 1), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": reps, "warmup": warm, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "torch.mm 8192 x 8192 x 8192 bf16 (hipBLASLt); torch SDPA (flash / mem-efficient "
+                               "backend) 880 x 19,360 keys x 24 heads x 128, bf16"},
+        "gemm_8192": {"us_per_call": round(us_mm, 1), "tflops": round(mm_tflops, 1),
+                      "pct_bf16_peak": round(100 * mm_tflops / PEAK_BF16_TFLOPS, 2)},
+        "sdpa_880x19360": {"us_per_call": round(us_sdpa, 1), "tflops": round(sdpa_tflops, 1),
+                           "pct_bf16_peak": round(100 * sdpa_tflops / PEAK_BF16_TFLOPS, 2)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.counters:
@@ -622,6 +680,9 @@ def main():
         return
     if args.workload in CONV_LAYERS:
         conv_workload(args)
+        return
+    if args.workload == "vendor_reference":
+        vendor_reference(args)
         return
     dev = torch.device("cuda:0")
     cfg = profile_config()
