@@ -20,9 +20,10 @@
 // buffers alternate; tile t+1 is in flight while tile t is computed, with
 // one barrier per tile.
 //
-// Products use v_mfma_f32_32x32x16_bf16 (32x32 output blocks; on gfx950 it
-// does twice the work of the 16x16x32 form in the same issue time, which
-// caps that form at half the matrix peak): per tile and wave
+// Products use v_mfma_f32_32x32x16_bf16 (32x32 output blocks: the matrix
+// units run it at the same FLOP rate as the 16x16x32 form, and per FLOP it
+// takes half the operand registers, so half the LDS operand reads): per tile
+// and wave
 //   S^T[64 keys x 32 queries] = K_tile Q^T      2 blocks x d/16 steps
 //   O^T[d x 32 queries]      += V^T_tile P^T    d/32 blocks x 4 steps
 // With the queries as the N columns, lane l holds the scores of query l % 32
