@@ -357,14 +357,16 @@ def rollout30x2(args):
     print(json.dumps(result), flush=True)
 
 
-def single_call_timing(heads=24, calls=50, warmup=5, peaky=True):
+def single_call_timing(heads=24, calls=50, warmup=5, peaky=True, spread=True):
     """One chunk-attention call shape on its own: 880 queries x 19,360 keys
     (chunk 19: sink 2640 + 18 x 880 window + 880 self), `heads` heads x 128.
     A 1-layer cache gets the sink and chunks 1..19 at step 0 from seeded
     N(0,1) bf16 inputs; with `peaky`, round(1% x 19,360) = 194 of the window's
     key rows (a seeded permutation over all 19,360 positions) are scaled by 4
     before RoPE, for a peaky softmax.  Then `calls` event-timed calls of chunk
-    19's attention on the launch stream after `warmup` untimed ones.
+    19's attention on the launch stream after `warmup` untimed ones (one event
+    pair around them all: the mean), and with `spread` the same number again
+    with an event pair around each call (median, p10, p90).
     heads = 3 is one GPU's share of 24 heads sharded 8 ways."""
     import torch
 
@@ -409,10 +411,28 @@ def single_call_timing(heads=24, calls=50, warmup=5, peaky=True):
     stop.record(stream)
     torch.cuda.synchronize()
     us = 1e3 * start.elapsed_time(stop) / calls
+    spread_us = None
+    if spread:
+        # the same calls again, an event pair around each one
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for a, b in pairs:
+            a.record(stream)
+            cache.chunk_attention(0, 0, 19, q_rot, out, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        each = sorted(1e3 * a.elapsed_time(b) for a, b in pairs)
+
+        def pct(q):
+            return round(each[min(len(each) - 1, int(q * (len(each) - 1) + 0.5))], 2)
+
+        spread_us = {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9),
+                     "note": "an event pair around each call (pair overhead included)"}
+
     flops = attn_flops(cfg, 19)
     tflops = flops / (us * 1e-6) / 1e12
     return {"us_per_call": round(us, 2), "tflops": round(tflops, 2),
             "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "launches_timed": calls,
+            "per_call_events_us": spread_us,
             "key_splits": cache.attention_splits(n1, total), "heads": heads,
             "inputs": ("N(0,1) bf16; 194 of the 19,360 window key rows scaled x4 before RoPE (peaky softmax)"
                        if peaky else "N(0,1) bf16")}
@@ -423,7 +443,7 @@ def attn880x19360(args, heads=24):
     the single peaky 880-query x 19,360-key call alone, `--steps` timed calls
     (also used for per-kernel counter runs, where the rollout's mix of call
     shapes would blur the counters)."""
-    r = single_call_timing(heads, calls=args.steps, warmup=args.warmup)
+    r = single_call_timing(heads, calls=args.steps, warmup=args.warmup, spread=False)
     print(json.dumps({
         "metric": "chunk-attn TFLOP/s, 880 queries x 19,360 keys",
         "value": r["tflops"],
