@@ -357,7 +357,7 @@ def rollout30x2(args):
     print(json.dumps(result), flush=True)
 
 
-def single_call_timing(heads=24, calls=50, warmup=5, peaky=True, spread=True):
+def single_call_timing(heads=24, calls=50, warmup=60, peaky=True, spread=True):
     """One chunk-attention call shape on its own: 880 queries x 19,360 keys
     (chunk 19: sink 2640 + 18 x 880 window + 880 self), `heads` heads x 128.
     A 1-layer cache gets the sink and chunks 1..19 at step 0 from seeded
@@ -366,7 +366,10 @@ def single_call_timing(heads=24, calls=50, warmup=5, peaky=True, spread=True):
     before RoPE, for a peaky softmax.  Then `calls` event-timed calls of chunk
     19's attention on the launch stream after `warmup` untimed ones (one event
     pair around them all: the mean), and with `spread` the same number again
-    with an event pair around each call (median, p10, p90).
+    with an event pair around each call (median, p10, p90).  The default
+    warm-up is long because a series of identical heavy calls first slows
+    down by up to a third (the clock drops under the sustained matrix load)
+    and settles again within about 50 calls.
     heads = 3 is one GPU's share of 24 heads sharded 8 ways."""
     import torch
 
