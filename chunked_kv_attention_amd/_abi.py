@@ -160,6 +160,12 @@ def _check(st: int, what: str):
         raise CkvError(st, what)
 
 
+def _same_device(t, arena, name):
+    """The kernels run on the arena's GPU: a tensor on another GPU is refused."""
+    if t.device != arena.device:
+        raise ValueError(f"{name} is on {t.device}, the arena on {arena.device}")
+
+
 class Cache:
     """One same-step K/V cache (sinks + per-(layer, step) rings) over a torch
     arena on the current device.  `dry=True` makes a host-only cache that
@@ -194,6 +200,7 @@ class Cache:
             raise TypeError(f"{name} must be a contiguous bf16 device tensor")
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        _same_device(t, self.arena, name)
         return t.data_ptr()
 
     def _stream(self, stream):
@@ -228,6 +235,7 @@ class Cache:
             raise TypeError(f"{name} must be a contiguous float32 device tensor")
         if g.numel() != width:
             raise ValueError(f"{name} has {g.numel()} values, expected {width}")
+        _same_device(g, self.arena, name)
         return g.data_ptr()
 
     def norm_rope_append(self, layer, step, chunk, q, k, v, q_gain, k_gain, eps, q_rot, stream=None):
@@ -373,6 +381,7 @@ class CausalConv:
             raise TypeError(f"{name} must be a contiguous bf16 device tensor")
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        _same_device(t, self.arena, name)
         return t.data_ptr()
 
     def _stream(self, stream):

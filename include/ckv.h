@@ -22,8 +22,11 @@
  *     0 and gh*gw for every later chunk.  Tokens are ordered frame-major,
  *     then patch row, then patch column.
  *   - Every tensor pointer is a DEVICE pointer on the current HIP device and
- *     must be 16-byte aligned.  The caller owns all device memory, including
- *     the cache arena; the library never allocates or frees device memory.
+ *     must be 16-byte aligned; the cache's arena must be on that device too
+ *     (with several GPUs, make the arena's device current before each call:
+ *     kernels launch on the current device).  The caller owns all device
+ *     memory, including the cache arena; the library never allocates or
+ *     frees device memory.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously; no call synchronises the host.
  *     Inputs must stay valid until the stream has passed the call.

@@ -23,7 +23,8 @@
  *     channels_last_3d order).  Weights are bf16 in Conv3d's own layout
  *     [C_out][C_in][kt][kh][kw]; bias is bf16 [C_out] or NULL (zero).
  *     Accumulation is float32; y is rounded to bf16 (nearest even) once.
- *   - Device pointers, 16-byte aligned; the caller owns all device memory,
+ *   - Device pointers on the current HIP device (the state arena's device),
+ *     16-byte aligned; the caller owns all device memory,
  *     including the state arena (ckv_conv_bytes); the library never
  *     allocates, frees or synchronises.  x and y must not overlap.
  *   - `stream` is a hipStream_t passed as void*; calls on one state object
