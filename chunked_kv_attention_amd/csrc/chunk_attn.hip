@@ -584,35 +584,50 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_kernel(AttnParams p) {
 }
 
 // Merge of the key splits: O = sum_j 2^(lse_j - M) O_j / sum_j 2^(lse_j - M),
-// M = max_j lse_j.  A thread takes 8 dims (16 bytes of each fp16 partial) of
-// one (query, head) row and loads every split's log-sum-exp and partial
-// before it uses any (MaxSplits bounds n_splits), so a row costs two memory
-// round trips whatever the split count.
-template <int D, int MaxSplits>
+// M = max_j lse_j.  G adjacent lanes share 8 dims (16 bytes of each fp16
+// partial) of one (query, head) row; lane g of the group takes splits g,
+// g + G, g + 2G, ... (MaxSplits / G of them), loading every one's
+// log-sum-exp and partial before it uses any, so a row costs two memory round
+// trips whatever the split count.  The group then takes its max of the
+// log-sum-exps and its sums with lane shuffles (a fixed order, so repeated
+// calls agree bit for bit), and lane 0 stores.  Many splits (few heads) get
+// G = 4: four times the threads of one lane per 8 dims, which would leave
+// most CUs idle at 3 heads.
+template <int D, int MaxSplits, int G>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
-  constexpr int TPR = D / 8;  // threads per (query, head) row
+  constexpr int TPR = D / 8;          // 16-byte pieces per (query, head) row
+  constexpr int PER = MaxSplits / G;  // splits per lane
+  static_assert(MaxSplits % G == 0 && 256 % (TPR * G) == 0, "groups tile the block");
   const long long rows = (long long)p.n_queries * p.num_heads;
-  const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  if (row >= rows) return;
-  const int c8 = threadIdx.x % TPR;
-  float lse[MaxSplits];
+  const int g = threadIdx.x % G;
+  const int c8 = (threadIdx.x / G) % TPR;
+  const long long row = (long long)blockIdx.x * (256 / (TPR * G)) + threadIdx.x / (TPR * G);
+  if (row >= rows) return;  // uniform over each group of G lanes (same row)
+  float lse[PER];
+  uint4 part[PER];
 #pragma unroll
-  for (int j = 0; j < MaxSplits; ++j) lse[j] = j < p.n_splits ? p.part_lse[j * rows + row] : -INFINITY;
-  uint4 part[MaxSplits];
+  for (int i = 0; i < PER; ++i) {
+    const int j = g + G * i;
+    lse[i] = j < p.n_splits ? p.part_lse[j * rows + row] : -INFINITY;
+  }
 #pragma unroll
-  for (int j = 0; j < MaxSplits; ++j)
-    part[j] = j < p.n_splits ? *reinterpret_cast<const uint4*>(p.part_o + (j * rows + row) * D + 8 * c8)
+  for (int i = 0; i < PER; ++i) {
+    const int j = g + G * i;
+    part[i] = j < p.n_splits ? *reinterpret_cast<const uint4*>(p.part_o + (j * rows + row) * D + 8 * c8)
                              : make_uint4(0, 0, 0, 0);
+  }
   float mx = lse[0];
 #pragma unroll
-  for (int j = 1; j < MaxSplits; ++j) mx = fmaxf(mx, lse[j]);
+  for (int i = 1; i < PER; ++i) mx = fmaxf(mx, lse[i]);
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   float wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < MaxSplits; ++j) {
-    const float w = j < p.n_splits ? __builtin_amdgcn_exp2f(lse[j] - mx) : 0.f;
+  for (int i = 0; i < PER; ++i) {
+    const float w = g + G * i < p.n_splits ? __builtin_amdgcn_exp2f(lse[i] - mx) : 0.f;
     wsum += w;
-    const uint32_t words[4] = {part[j].x, part[j].y, part[j].z, part[j].w};
+    const uint32_t words[4] = {part[i].x, part[i].y, part[i].z, part[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const half2 v = __builtin_bit_cast(half2, words[e]);
@@ -620,6 +635,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
       acc[2 * e + 1] += w * (float)v[1];
     }
   }
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) {
+    wsum += __shfl_xor(wsum, off, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+  if (g != 0) return;
   const float inv = 1.f / wsum;
   uint32_t packed[4];
 #pragma unroll
@@ -630,15 +652,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   *reinterpret_cast<uint4*>(p.out + row * D + 8 * c8) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
+template <int D, int MaxSplits, int G>
+void launch_combine_with(const AttnParams& p, hipStream_t s) {
+  const int blocks = (int)(((long long)p.n_queries * p.num_heads * (D / 8) * G + 255) / 256);
+  hipLaunchKernelGGL((attn_combine_kernel<D, MaxSplits, G>), dim3(blocks), dim3(256), 0, s, p);
+}
+
 template <int D>
 void launch_combine(const AttnParams& p, hipStream_t s) {
-  const int blocks = (int)(((long long)p.n_queries * p.num_heads * (D / 8) + 255) / 256);
   if (p.n_splits <= 4)
-    hipLaunchKernelGGL((attn_combine_kernel<D, 4>), dim3(blocks), dim3(256), 0, s, p);
+    launch_combine_with<D, 4, 1>(p, s);
   else if (p.n_splits <= 8)
-    hipLaunchKernelGGL((attn_combine_kernel<D, 8>), dim3(blocks), dim3(256), 0, s, p);
+    launch_combine_with<D, 8, 2>(p, s);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<D, kAttnMaxSplits>), dim3(blocks), dim3(256), 0, s, p);
+    launch_combine_with<D, kAttnMaxSplits, 4>(p, s);
 }
 
 }  // namespace

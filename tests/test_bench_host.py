@@ -56,7 +56,7 @@ def test_counter_summary_scales_by_the_copy_and_checks_the_source(tmp_path, monk
     counter reads for the 1 GiB copy; the traffic is dropped when the kernel
     source no longer matches the summary's hash."""
     attn = "void ckv::(anonymous namespace)::chunk_attn_kernel<128>(ckv::AttnParams)"
-    merge = "void ckv::(anonymous namespace)::attn_combine_kernel<128, 4>(ckv::AttnParams)"
+    merge = "void ckv::(anonymous namespace)::attn_combine_kernel<128, 4, 1>(ckv::AttnParams)"
     fetch = tmp_path / "fetch.csv"
     write = tmp_path / "write.csv"
     # the copy reads 1 GiB: FETCH_SIZE reports half of it, WRITE_SIZE all of it
