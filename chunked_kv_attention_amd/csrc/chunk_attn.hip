@@ -20,10 +20,12 @@
 // buffers alternate; tile t+1 is in flight while tile t is computed, with
 // one barrier per tile.
 //
-// Products use v_mfma_f32_32x32x16_bf16 (32x32 output blocks: the matrix
-// units run it at the same FLOP rate as the 16x16x32 form, and per FLOP it
-// takes half the operand registers, so half the LDS operand reads): per tile
-// and wave
+// Products use v_mfma_f32_32x32x16_bf16 (32x32 output blocks; the matrix
+// units run it at the same FLOP rate as the 16x16x32 form, and a wave's
+// operand bytes depend on its tile, not on the form, but its accumulator
+// layout gives a lane 16 scores of a single query, so the softmax needs only
+// a two-lane reduction and the weights go from registers straight into the
+// B operand of the PV product): per tile and wave
 //   S^T[64 keys x 32 queries] = K_tile Q^T      2 blocks x d/16 steps
 //   O^T[d x 32 queries]      += V^T_tile P^T    d/32 blocks x 4 steps
 // With the queries as the N columns, lane l holds the scores of query l % 32
