@@ -335,6 +335,24 @@ def test_four_key_splits_every_element():
     print(f"4-split d=64: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
 
 
+def test_two_to_fourteen_key_splits_every_element():
+    """1 head x 64, 16 x 16 grid (256 queries: 2 query tiles), first chunk of
+    3 frames, window 24: chunk c (1..25) sees 768 + 256 c keys, so the split
+    count climbs from 2 to 14 one step every two chunks.  That runs all three
+    merge variants (up to 4 splits, one lane per 8 dims; 5..8 splits, lane
+    pairs; 9..14, groups of four lanes, some of whose lanes hold no split);
+    every output element of every call against the oracle."""
+    cfg = C.Config(1, 1, 1, 64, 16, 16, 3, 24, 26)
+    r = G.Rollout(cfg, base_seed=14)
+    splits = [r.cache.attention_splits(256, 768 + 256 * c) for c in range(1, 26)]
+    print(f"splits per chunk: {splits}")
+    assert set(range(5, 9)) <= set(splits), splits
+    assert any(p > 8 and p % 4 for p in splits), splits
+    r.run_first_chunk()
+    r.run_chunks(range(1, 26))
+    print(f"2..14 splits d=64: max abs {r.worst[0]:.3e} rel L2 {r.worst[1]:.3e}")
+
+
 @pytest.mark.timeout(600)
 def test_rollout_one_layer_profile():
     """29 chunks x 4 steps, 24 x 128, 880 tokens per chunk after the 2640-token
